@@ -1,0 +1,45 @@
+"""Readers for the text fixtures under tests/golden/."""
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def e4m3_values():
+    rows = []
+    with open(os.path.join(GOLDEN, "e4m3fn_values.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            rows.append((float(tok[0]), int(tok[1], 16)))
+    return rows
+
+
+def worked_tiles():
+    tiles, cur = [], None
+    with open(os.path.join(GOLDEN, "worked_tiles.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0] == "tile":
+                cur = {"name": tok[1], "rows": int(tok[2]), "cols": int(tok[3])}
+                tiles.append(cur)
+            elif tok[0] == "x":
+                cur["x"] = np.array([float(t) for t in tok[1:]], dtype=np.float32).reshape(cur["rows"], cur["cols"])
+            elif tok[0] == "scale_bits":
+                cur["scale_bits"] = int(tok[1], 16)
+            elif tok[0] == "bytes":
+                cur["bytes"] = np.array([int(t, 16) for t in tok[1:]], dtype=np.uint8).reshape(cur["rows"], cur["cols"])
+    return tiles
+
+
+def f32_to_bf16_bits_exact(x):
+    """BF16 bit patterns of float32 values that are exactly representable in BF16."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exactly representable in BF16"
+    return (u >> 16).astype(np.uint16)
