@@ -1,0 +1,197 @@
+"""Benchmark of the parameter-preparation hot path on one MI355X.
+
+One step = one wt_prepare replay over the whole workload (shard gather +
+projection fusion + 128x128-tile E4M3 quantization + packing into the
+destination region), inputs already resident in HBM, destination written in
+place (zero-copy). Default workload: one GPU's share of a Kimi-K2-shaped MoE
+layer (96 experts, gate_up [4096x7168] fused from w1/w3, w2 [7168x2048],
+8 row shards each; 8.46 GB of BF16).
+
+Prints ONE JSON line on stdout. The CPU baseline is the oracle (plain C,
+test infrastructure) run over the same workload bytes on the host's cores,
+and its image is compared byte for byte with the GPU's output.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="kimi_k2_moe",
+                    choices=["kimi_k2_moe", "dense_7b", "dense_layer_h1024", "ragged_stress"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = min(16, cores))")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters for the current kernel")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the preparation path does not "
+              "shard across GPUs in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    from bf16_fp8_weight_amd import workloads as W
+    from bf16_fp8_weight_amd import wt
+
+    torch.cuda.set_device(0)
+    make = W.WORKLOADS[args.workload]
+    t0 = time.time()
+    wl = make(device="cuda")
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: {len(wl.outputs)} outputs, {wl.input_bytes / 1e9:.3f} GB BF16 in, "
+        f"{wl.n_tiles} tiles, generated in {time.time() - t0:.1f}s")
+
+    dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    plan = wt.Plan(wl, dst)
+    info = plan.info()
+    log(f"plan: {info}")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        plan.prepare(sp)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_begin = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        plan.prepare(sp)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_begin
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = t_total / args.steps * 1e3
+
+    in_bytes = wl.input_bytes
+    alg_bytes = wl.algorithmic_bytes
+    value = in_bytes / (t_total / args.steps) / 1e9          # prepared BF16 GB/s, whole job
+    achieved = alg_bytes / avg_launch_s / 1e9                # algorithmic HBM GB/s of the launch
+    log(f"steps {args.steps}: {ms_per_step:.4f} ms/step wall, launch avg {avg_launch_s * 1e3:.4f} ms "
+        f"(min {min(launch_ms):.4f}, max {max(launch_ms):.4f}); prepared {value:.1f} GB/s; "
+        f"HBM {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.3f} of peak")
+
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha():
+            traffic = tj.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    cpu = None
+    verified = None
+    if not args.no_cpu_baseline:
+        cpu, verified = _cpu_baseline(wl, dst, args.cpu_threads)
+
+    line = {
+        "metric": "prepared BF16 GB/s (shard gather+fuse+FP8 quant+pack) and % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->fp8e4m3fn (fp32 scale math)",
+        "data": "synthetic: seeded N(0, 0.02) BF16, random weights of the stated shapes",
+        "config": {
+            "workload": wl.name,
+            "outputs": len(wl.outputs),
+            "input_bytes": in_bytes,
+            "output_bytes": wl.output_bytes,
+            "tiles": wl.n_tiles,
+            "shards_per_tensor": 8,
+            "dst_mode": "zero-copy, device-resident shards",
+        },
+        "pct_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_ms": round(avg_launch_s * 1e3, 5),
+            "launches_per_step": info["n_launches"],
+        },
+        "cpu_baseline": cpu,
+        "verified_vs_oracle": verified,
+    }
+    print(json.dumps(line), flush=True)
+    plan.close()
+    return 0 if verified in (None, True) else 1
+
+
+def _kernel_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("prep_kernels.hip", "wt_internal.h"):
+        with open(os.path.join(ROOT, "bf16_fp8_weight_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _cpu_baseline(wl, dst, threads):
+    """Times the oracle over the whole workload on the host's cores (threads
+    over outputs) and compares its image with the GPU's output."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    import oracle_glue
+
+    oracle.build(force=False)
+    n = threads or min(16, os.cpu_count() or 1)
+    t0 = time.time()
+    outs = oracle_glue.oracle_outputs(wl)  # D2H of the shard bytes (not timed)
+    log(f"cpu baseline: copied {wl.input_bytes / 1e9:.2f} GB of shards to host in {time.time() - t0:.1f}s")
+    img = np.full(wl.dst_bytes, 0xA5, dtype=np.uint8)
+    t1 = time.perf_counter()
+    with ThreadPoolExecutor(n) as ex:
+        list(ex.map(lambda o: oracle.prepare([o], wl.dst_bytes, img), outs))
+    dt = time.perf_counter() - t1
+    got = dst.cpu().numpy()
+    ok = bool(np.array_equal(got, img))
+    log(f"cpu baseline: oracle {dt:.2f}s on {n} threads = {wl.input_bytes / dt / 1e9:.3f} GB/s; GPU output "
+        f"{'identical to' if ok else 'DIFFERS from'} the oracle image")
+    return {
+        "value": round(wl.input_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": n,
+        "kind": "oracle",
+        "sample": f"the whole workload ({len(outs)} outputs, {wl.input_bytes} B BF16), one thread per output",
+        "seconds": round(dt, 2),
+    }, ok
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,541 @@
+// runtime.cpp -- C ABI of libwt.so: plan creation (device tables, staging,
+// streams), replay, teardown, and the element-function check entry points.
+//
+// Replay follows "Weight transfer for RL post-training in under 2 seconds",
+// section "Task pipeline": each stage keeps a FIFO of tasks and a task moves
+// to the next stage's queue when it finishes the current one. Here each stage
+// is an in-order HIP stream (host-to-device copy, prepare, destination copy);
+// a chunk of tasks enters the next stage's stream behind an event recorded
+// when it left the previous one, and a chunk's host-to-device copy waits for
+// the release of the earlier chunk whose staging slot it reuses, which keeps
+// in-flight staging under the watermark (section "GPU memory usage control").
+// Everything is enqueued asynchronously; the host never polls.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+#include "wt.h"
+
+namespace wt {
+hipError_t launch_batch(const LaunchTables &T, hipStream_t stream);
+hipError_t launch_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, uint8_t *out, int variant,
+                                  hipStream_t stream);
+hipError_t launch_cast_range(uint32_t first, uint64_t count, uint8_t *out, hipStream_t stream);
+}  // namespace wt
+
+using namespace wt;
+
+struct wt_plan {
+  Layout L;
+  int device = 0;
+  uint8_t *dst = nullptr;
+  size_t dst_bytes = 0;
+  int32_t dst_kind = WT_MEM_DEVICE;
+  bool pipeline = false;
+
+  uint8_t *tables = nullptr;  // every batch's device tables, one allocation
+  uint8_t *staging = nullptr;
+  std::vector<LaunchTables> batches;  // [0] = direct batch when present, then one per chunk
+  int direct_batch = -1;
+  int first_chunk_batch = 0;
+
+  hipStream_t s_h2d = nullptr, s_prep = nullptr, s_out = nullptr;
+  std::vector<hipEvent_t> ev_h2d, ev_prep, ev_rel;
+  hipEvent_t ev_start = nullptr, ev_out_end = nullptr, ev_done = nullptr;
+  bool has_prev = false;
+
+  std::atomic<bool> busy{false};
+  mutable std::mutex err_mu;
+  std::string last_error;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+void set_err(wt_plan *p, const std::string &m) {
+  if (p) {
+    std::lock_guard<std::mutex> g(p->err_mu);
+    p->last_error = m;
+  } else {
+    g_last_error = m;
+  }
+}
+
+std::string hip_msg(const char *what, hipError_t e) {
+  return std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+}
+
+#define HIP_OR(plan, expr)                               \
+  do {                                                   \
+    hipError_t e_ = (expr);                              \
+    if (e_ != hipSuccess) {                              \
+      set_err((plan), hip_msg(#expr, e_));               \
+      return WT_E_HIP;                                   \
+    }                                                    \
+  } while (0)
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess) ok = true;
+    if (dev >= 0 && dev != prev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (ok) (void)hipSetDevice(prev);
+  }
+};
+
+wt_plan_options resolve_opts(const wt_plan_options *o) {
+  wt_plan_options d;
+  wt_plan_options_init(&d);
+  if (!o) return d;
+  wt_plan_options r = *o;
+  if (r.watermark_bytes == 0) r.watermark_bytes = d.watermark_bytes;
+  return r;
+}
+
+// Checks that [p, p + bytes) lies in one allocation of the expected kind.
+wt_status check_memory(const void *p, uint64_t bytes, int32_t kind, int device, const std::string &what,
+                       std::string *err) {
+  if (bytes == 0) return WT_OK;
+  hipPointerAttribute_t a;
+  std::memset(&a, 0, sizeof a);
+  hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *err = what + ": pointer is not HIP device or pinned host memory";
+    return WT_E_INVAL;
+  }
+  if (kind == WT_MEM_DEVICE) {
+    if (a.type != hipMemoryTypeDevice) {
+      *err = what + ": expected device memory";
+      return WT_E_INVAL;
+    }
+    if (a.device != device) {
+      *err = what + ": device memory of another GPU";
+      return WT_E_INVAL;
+    }
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) == hipSuccess && base) {
+      const uint64_t lo = (uint64_t)(uintptr_t)base, hi = lo + size;
+      if ((uint64_t)(uintptr_t)p + bytes > hi) {
+        *err = what + ": range runs past the end of its allocation";
+        return WT_E_RANGE;
+      }
+    } else {
+      (void)hipGetLastError();
+    }
+  } else {
+    if (a.type != hipMemoryTypeHost) {
+      *err = what + ": expected pinned host memory";
+      return WT_E_INVAL;
+    }
+  }
+  return WT_OK;
+}
+
+struct RealAddr : BatchAddr {
+  const Layout *L;
+  const Chunk *C;  // null for the direct batch
+  uint64_t dst, staging;
+  uint64_t seg_src(int32_t k, int32_t o, int32_t s) const override {
+    if (C && C->h2d) return staging + (uint64_t)C->slot_off + (uint64_t)C->seg_stage[k][s];
+    return (uint64_t)(uintptr_t)L->outs[o].segs[s].src;
+  }
+  uint64_t data_dst(int32_t k, int32_t o) const override {
+    if (C && C->data_stage[k] >= 0) return staging + (uint64_t)C->slot_off + (uint64_t)C->data_stage[k];
+    return dst + L->outs[o].dst_off;
+  }
+  uint64_t scale_dst(int32_t k, int32_t o) const override {
+    if (C && C->scale_stage[k] >= 0) return staging + (uint64_t)C->slot_off + (uint64_t)C->scale_stage[k];
+    return dst + L->outs[o].scale_off;
+  }
+};
+
+size_t pad256(size_t x) { return (x + 255) & ~size_t(255); }
+
+template <class T>
+size_t blob_bytes(const std::vector<T> &v) {
+  return pad256(v.size() * sizeof(T));
+}
+
+void destroy_resources(wt_plan *p) {
+  if (p->s_prep) (void)hipStreamSynchronize(p->s_prep);
+  if (p->s_out) (void)hipStreamSynchronize(p->s_out);
+  if (p->s_h2d) (void)hipStreamSynchronize(p->s_h2d);
+  for (auto *v : {&p->ev_h2d, &p->ev_prep, &p->ev_rel})
+    for (hipEvent_t e : *v)
+      if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : {p->ev_start, p->ev_out_end, p->ev_done})
+    if (e) (void)hipEventDestroy(e);
+  for (hipStream_t s : {p->s_h2d, p->s_prep, p->s_out})
+    if (s) (void)hipStreamDestroy(s);
+  if (p->tables) (void)hipFree(p->tables);
+  if (p->staging) (void)hipFree(p->staging);
+}
+
+wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt_plan_options &opts) {
+  std::string err;
+  // memory of every shard and of the destination region
+  {
+    wt_status st = check_memory(p->dst, p->dst_bytes, p->dst_kind, p->device, "destination region", &err);
+    if (st != WT_OK) {
+      set_err(p, err);
+      return st;
+    }
+    if ((uintptr_t)p->dst % 16) {
+      set_err(p, "destination region base not 16-byte aligned");
+      return WT_E_ALIGN;
+    }
+    for (size_t i = 0; i < n_tasks; ++i)
+      for (int32_t k = 0; k < tasks[i].n_shards; ++k) {
+        const wt_shard &s = tasks[i].shards[k];
+        st = check_memory(s.ptr, 2ull * (uint64_t)s.rows * (uint64_t)tasks[i].cols, tasks[i].shard_mem, p->device,
+                          "task " + std::to_string(i) + " shard " + std::to_string(k), &err);
+        if (st != WT_OK) {
+          set_err(p, err);
+          return st;
+        }
+      }
+  }
+  const Layout &L = p->L;
+  p->pipeline = !L.chunks.empty();
+
+  if (L.staging_bytes > 0) HIP_OR(p, hipMalloc((void **)&p->staging, (size_t)L.staging_bytes));
+
+  // host tables of every batch
+  std::vector<HostTables> hts;
+  RealAddr ra;
+  ra.L = &L;
+  ra.dst = (uint64_t)(uintptr_t)p->dst;
+  ra.staging = (uint64_t)(uintptr_t)p->staging;
+  if (!L.direct.empty()) {
+    ra.C = nullptr;
+    hts.emplace_back();
+    build_tables(L, L.direct, ra, &hts.back());
+    p->direct_batch = 0;
+  }
+  p->first_chunk_batch = (int)hts.size();
+  for (const Chunk &C : L.chunks) {
+    ra.C = &C;
+    hts.emplace_back();
+    build_tables(L, C.outputs, ra, &hts.back());
+  }
+  size_t total = 0;
+  for (const HostTables &t : hts)
+    total += blob_bytes(t.outs) + blob_bytes(t.segs) + blob_bytes(t.fast) + blob_bytes(t.general) +
+             blob_bytes(t.copies);
+  std::vector<uint8_t> blob(std::max<size_t>(total, 256), 0);
+  if (total > 0) HIP_OR(p, hipMalloc((void **)&p->tables, total));
+  size_t off = 0;
+  for (const HostTables &t : hts) {
+    LaunchTables T{};
+    auto put = [&](const auto &v) -> uint64_t {
+      using E = typename std::decay_t<decltype(v)>::value_type;
+      const uint64_t dev = (uint64_t)(uintptr_t)(p->tables + off);
+      if (!v.empty()) std::memcpy(blob.data() + off, v.data(), v.size() * sizeof(E));
+      off += blob_bytes(v);
+      return dev;
+    };
+    T.outs = (const DevOut *)(uintptr_t)put(t.outs);
+    T.segs = (const DevSeg *)(uintptr_t)put(t.segs);
+    T.fast_tiles = (const TileItem *)(uintptr_t)put(t.fast);
+    T.general_tiles = (const TileItem *)(uintptr_t)put(t.general);
+    T.copies = (const CopyItem *)(uintptr_t)put(t.copies);
+    if (t.fast.size() > UINT32_MAX / 2 || t.general.size() > UINT32_MAX / 2 || t.copies.size() > UINT32_MAX / 2) {
+      set_err(p, "work list too large for one launch");
+      return WT_E_INVAL;
+    }
+    T.n_fast = (uint32_t)t.fast.size();
+    T.n_general = (uint32_t)t.general.size();
+    T.n_copies = (uint32_t)t.copies.size();
+    p->batches.push_back(T);
+  }
+  if (total > 0) HIP_OR(p, hipMemcpy(p->tables, blob.data(), total, hipMemcpyHostToDevice));
+
+  if (p->pipeline) {
+    HIP_OR(p, hipStreamCreateWithFlags(&p->s_h2d, hipStreamNonBlocking));
+    HIP_OR(p, hipStreamCreateWithFlags(&p->s_prep, hipStreamNonBlocking));
+    HIP_OR(p, hipStreamCreateWithFlags(&p->s_out, hipStreamNonBlocking));
+    const size_t nc = L.chunks.size();
+    p->ev_h2d.assign(nc, nullptr);
+    p->ev_prep.assign(nc, nullptr);
+    p->ev_rel.assign(nc, nullptr);
+    for (size_t c = 0; c < nc; ++c) {
+      HIP_OR(p, hipEventCreateWithFlags(&p->ev_h2d[c], hipEventDisableTiming));
+      HIP_OR(p, hipEventCreateWithFlags(&p->ev_prep[c], hipEventDisableTiming));
+      HIP_OR(p, hipEventCreateWithFlags(&p->ev_rel[c], hipEventDisableTiming));
+    }
+    HIP_OR(p, hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming));
+    HIP_OR(p, hipEventCreateWithFlags(&p->ev_out_end, hipEventDisableTiming));
+    HIP_OR(p, hipEventCreateWithFlags(&p->ev_done, hipEventDisableTiming));
+  }
+  return WT_OK;
+}
+
+wt_status prepare_impl(wt_plan *p, hipStream_t user) {
+  const Layout &L = p->L;
+  if (!p->pipeline) {
+    HIP_OR(p, launch_batch(p->batches[p->direct_batch], user));
+    return WT_OK;
+  }
+  const bool staged = L.dst_mode == WT_DST_STAGED;
+  const hipMemcpyKind out_kind = p->dst_kind == WT_MEM_DEVICE ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
+
+  // Order after the caller's prior work and after this plan's previous replay.
+  HIP_OR(p, hipEventRecord(p->ev_start, user));
+  for (hipStream_t s : {p->s_h2d, p->s_prep, p->s_out}) {
+    HIP_OR(p, hipStreamWaitEvent(s, p->ev_start, 0));
+    if (p->has_prev) HIP_OR(p, hipStreamWaitEvent(s, p->ev_done, 0));
+  }
+  if (p->direct_batch >= 0) HIP_OR(p, launch_batch(p->batches[p->direct_batch], p->s_prep));
+
+  for (size_t c = 0; c < L.chunks.size(); ++c) {
+    const Chunk &C = L.chunks[c];
+    if (C.h2d) {
+      // stage 1: host-to-device copy, admitted once the slot it reuses is released
+      if (C.wait_for >= 0) HIP_OR(p, hipStreamWaitEvent(p->s_h2d, p->ev_rel[C.wait_for], 0));
+      for (const H2DCopy &h : C.h2d_copies)
+        HIP_OR(p, hipMemcpyAsync(p->staging + C.slot_off + h.stage_off, h.src, (size_t)h.bytes,
+                                 hipMemcpyHostToDevice, p->s_h2d));
+      HIP_OR(p, hipEventRecord(p->ev_h2d[c], p->s_h2d));
+      HIP_OR(p, hipStreamWaitEvent(p->s_prep, p->ev_h2d[c], 0));
+    } else if (C.wait_for >= 0) {
+      HIP_OR(p, hipStreamWaitEvent(p->s_prep, p->ev_rel[C.wait_for], 0));
+    }
+    // stage 2: preparation (one launch over the chunk's work list)
+    HIP_OR(p, launch_batch(p->batches[p->first_chunk_batch + c], p->s_prep));
+    HIP_OR(p, hipEventRecord(p->ev_prep[c], p->s_prep));
+    if (staged) {
+      // stage 3: staging -> destination region (the emulated one-sided write)
+      HIP_OR(p, hipStreamWaitEvent(p->s_out, p->ev_prep[c], 0));
+      for (const DstCopy &d : C.dst_copies)
+        HIP_OR(p, hipMemcpyAsync(p->dst + d.dst_off, p->staging + C.slot_off + d.stage_off, (size_t)d.bytes,
+                                 out_kind, p->s_out));
+      HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_out));
+    } else {
+      HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_prep));
+    }
+  }
+  // join: everything done -> ev_done on s_prep -> the caller's stream
+  HIP_OR(p, hipEventRecord(p->ev_out_end, p->s_out));
+  HIP_OR(p, hipStreamWaitEvent(p->s_prep, p->ev_out_end, 0));
+  HIP_OR(p, hipEventRecord(p->ev_done, p->s_prep));
+  HIP_OR(p, hipStreamWaitEvent(user, p->ev_done, 0));
+  p->has_prev = true;
+  return WT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void wt_plan_options_init(wt_plan_options *opts) {
+  if (!opts) return;
+  std::memset(opts, 0, sizeof *opts);
+  opts->watermark_bytes = 256ull << 20;
+  opts->chunk_bytes = 0;
+  opts->dst_write_mode = WT_DST_ZERO_COPY;
+  opts->device = -1;
+}
+
+wt_status wt_plan_check(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, int32_t dst_kind,
+                        const wt_plan_options *opts, wt_plan_info *info) {
+  try {
+    const wt_plan_options o = resolve_opts(opts);
+    Layout L;
+    std::string err;
+    wt_status st = build_layout(tasks, n_tasks, dst_bytes, dst_kind, o, &L, &err);
+    if (st != WT_OK) {
+      set_err(nullptr, err);
+      return st;
+    }
+    if (info) *info = L.info;
+    return WT_OK;
+  } catch (const std::bad_alloc &) {
+    set_err(nullptr, "host allocation failed");
+    return WT_E_NOMEM;
+  } catch (...) {
+    set_err(nullptr, "internal error");
+    return WT_E_INVAL;
+  }
+}
+
+wt_status wt_plan_schedule(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, int32_t dst_kind,
+                           const wt_plan_options *opts, wt_sched_op *ops, size_t max_ops, size_t *n_ops) {
+  try {
+    if (!n_ops) return WT_E_INVAL;
+    const wt_plan_options o = resolve_opts(opts);
+    Layout L;
+    std::string err;
+    wt_status st = build_layout(tasks, n_tasks, dst_bytes, dst_kind, o, &L, &err);
+    if (st != WT_OK) {
+      set_err(nullptr, err);
+      return st;
+    }
+    std::vector<wt_sched_op> v;
+    schedule_ops(L, &v);
+    *n_ops = v.size();
+    if (ops)
+      for (size_t i = 0; i < v.size() && i < max_ops; ++i) ops[i] = v[i];
+    return WT_OK;
+  } catch (const std::bad_alloc &) {
+    set_err(nullptr, "host allocation failed");
+    return WT_E_NOMEM;
+  } catch (...) {
+    set_err(nullptr, "internal error");
+    return WT_E_INVAL;
+  }
+}
+
+wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
+                         const wt_plan_options *opts, wt_plan **out) {
+  if (!out) return WT_E_INVAL;
+  *out = nullptr;
+  wt_plan *p = nullptr;
+  try {
+    const wt_plan_options o = resolve_opts(opts);
+    if (!dst || dst_bytes == 0) {
+      set_err(nullptr, "destination region is empty");
+      return WT_E_INVAL;
+    }
+    p = new wt_plan();
+    std::string err;
+    wt_status st = build_layout(tasks, n_tasks, dst_bytes, dst_kind, o, &p->L, &err);
+    if (st != WT_OK) {
+      set_err(nullptr, err);
+      delete p;
+      return st;
+    }
+    int dev = o.device;
+    if (dev < 0) {
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) {
+        set_err(nullptr, hip_msg("hipGetDevice", e));
+        delete p;
+        return WT_E_HIP;
+      }
+    }
+    p->device = dev;
+    p->dst = (uint8_t *)dst;
+    p->dst_bytes = dst_bytes;
+    p->dst_kind = dst_kind;
+    DeviceGuard guard(dev);
+    st = create_impl(p, tasks, n_tasks, o);
+    if (st != WT_OK) {
+      set_err(nullptr, p->last_error);
+      destroy_resources(p);
+      delete p;
+      return st;
+    }
+    *out = p;
+    return WT_OK;
+  } catch (const std::bad_alloc &) {
+    set_err(nullptr, "host allocation failed");
+    if (p) {
+      destroy_resources(p);
+      delete p;
+    }
+    return WT_E_NOMEM;
+  } catch (...) {
+    set_err(nullptr, "internal error");
+    if (p) {
+      destroy_resources(p);
+      delete p;
+    }
+    return WT_E_INVAL;
+  }
+}
+
+wt_status wt_prepare(wt_plan *plan, void *stream) {
+  if (!plan) return WT_E_INVAL;
+  bool expected = false;
+  if (!plan->busy.compare_exchange_strong(expected, true)) {
+    set_err(plan, "wt_prepare already running on this plan");
+    return WT_E_STATE;
+  }
+  wt_status st;
+  try {
+    DeviceGuard guard(plan->device);
+    st = prepare_impl(plan, (hipStream_t)stream);
+  } catch (...) {
+    set_err(plan, "internal error");
+    st = WT_E_INVAL;
+  }
+  plan->busy.store(false);
+  return st;
+}
+
+wt_status wt_plan_get_info(const wt_plan *plan, wt_plan_info *info) {
+  if (!plan || !info) return WT_E_INVAL;
+  *info = plan->L.info;
+  return WT_OK;
+}
+
+void wt_plan_destroy(wt_plan *plan) {
+  if (!plan) return;
+  {
+    DeviceGuard guard(plan->device);
+    destroy_resources(plan);
+  }
+  delete plan;
+}
+
+const char *wt_status_str(int status) {
+  switch (status) {
+    case WT_OK: return "WT_OK";
+    case WT_E_INVAL: return "WT_E_INVAL: malformed task table or argument";
+    case WT_E_RANGE: return "WT_E_RANGE: range outside the destination region or allocation";
+    case WT_E_OVERLAP: return "WT_E_OVERLAP: destination ranges overlap";
+    case WT_E_ALIGN: return "WT_E_ALIGN: misaligned pointer or offset";
+    case WT_E_NOMEM: return "WT_E_NOMEM: allocation failed";
+    case WT_E_HIP: return "WT_E_HIP: HIP runtime error";
+    case WT_E_WATERMARK: return "WT_E_WATERMARK: watermark below one output's staging need";
+    case WT_E_STATE: return "WT_E_STATE: plan busy";
+    default: return "unknown status";
+  }
+}
+
+const char *wt_plan_last_error(const wt_plan *plan) {
+  if (!plan) return g_last_error.c_str();
+  std::lock_guard<std::mutex> g(plan->err_mu);
+  // the string lives in the plan; valid until the next error on it or destroy
+  return plan->last_error.c_str();
+}
+
+wt_status wt_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, int32_t path, uint8_t *out, void *stream) {
+  if (n_amax < 0 || n_amax > (int64_t)1 << 20 || (path != 0 && path != 1)) return WT_E_INVAL;
+  if (n_amax == 0) return WT_OK;
+  if (!amax_bits || !out) return WT_E_INVAL;
+  hipError_t e = launch_quantize_domain(amax_bits, n_amax, out, path, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_err(nullptr, hip_msg("quantize_domain launch", e));
+    return WT_E_HIP;
+  }
+  return WT_OK;
+}
+
+wt_status wt_cast_f32_range(uint32_t first, uint64_t count, uint8_t *out, void *stream) {
+  if (count > (1ull << 32)) return WT_E_INVAL;
+  if (count == 0) return WT_OK;
+  if (!out) return WT_E_INVAL;
+  hipError_t e = launch_cast_range(first, count, out, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_err(nullptr, hip_msg("cast_range launch", e));
+    return WT_E_HIP;
+  }
+  return WT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// wt_internal.h -- descriptor tables shared by the host plan builder and the
+// HIP kernels of libwt.so. Plain structs, identical layout on host and device.
+#pragma once
+
+#include <cstdint>
+
+namespace wt {
+
+constexpr int kTile = 128;            // FP8 scale tile edge (128 x 128 elements)
+constexpr int kBlock = 256;           // threads per workgroup (4 wave64)
+constexpr uint32_t kCopyItemMax = 16384;  // bytes per copy work item (one wave each)
+constexpr int kCopiesPerBlock = kBlock / 64;
+
+// Output flags.
+enum : int32_t {
+  kOutFast = 1,  // cols % 8 == 0, data base 8-byte aligned, every segment 16-byte aligned
+};
+
+// One FP8 output tensor of a launch.
+struct DevOut {
+  uint64_t q;       // address of FP8 byte (0, 0) of the output
+  uint64_t s;       // address of the fp32 scale grid
+  int64_t rows;     // R (fused rows)
+  int32_t cols;     // C
+  int32_t tiles_c;  // ceil(C / 128)
+  int32_t flags;
+  int32_t pad0;
+  int64_t pad1;
+};
+static_assert(sizeof(DevOut) == 48, "DevOut layout");
+
+// A run of output rows [row0, row_end) read from one shard, rows contiguous
+// with stride cols (BF16). src is the address of output row row0.
+struct DevSeg {
+  uint64_t src;
+  int64_t row0;
+  int64_t row_end;
+  int64_t pad;
+};
+static_assert(sizeof(DevSeg) == 32, "DevSeg layout");
+
+// One 128 x 128 tile of an FP8 output. seg = index of the first segment of
+// the output that overlaps the tile's rows.
+struct TileItem {
+  uint32_t out;
+  uint32_t tile_row;
+  uint32_t tile_col;
+  uint32_t seg;
+};
+static_assert(sizeof(TileItem) == 16, "TileItem layout");
+
+// One byte-range copy (BF16 pass-through). width = 16, 4 or 2: src, dst and
+// bytes are all multiples of width.
+struct CopyItem {
+  uint64_t src;
+  uint64_t dst;
+  uint32_t bytes;
+  uint32_t width;
+  uint64_t pad;
+};
+static_assert(sizeof(CopyItem) == 32, "CopyItem layout");
+
+// Device tables of one launch batch.
+struct LaunchTables {
+  const DevOut *outs;
+  const DevSeg *segs;
+  const TileItem *fast_tiles;     // tiles of kOutFast outputs
+  const TileItem *general_tiles;  // tiles of the other outputs
+  const CopyItem *copies;
+  uint32_t n_fast;
+  uint32_t n_general;
+  uint32_t n_copies;
+  uint32_t pad;
+};
+
+}  // namespace wt

@@ -1,0 +1,263 @@
+"""ctypes binding of libwt.so (C ABI in include/wt.h), same names as the C calls.
+
+Argument marshalling only: every step of the preparation runs in the
+library's HIP kernels. PyTorch is used by callers for device memory and
+streams; this module passes raw addresses. Importing it raises if libwt.so has
+not been built, so no caller can silently run without the GPU library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libwt.so")
+
+WT_OK = 0
+WT_E_INVAL, WT_E_RANGE, WT_E_OVERLAP, WT_E_ALIGN, WT_E_NOMEM, WT_E_HIP, WT_E_WATERMARK, WT_E_STATE = range(1, 9)
+WT_FP8_E4M3FN_B128 = 0
+WT_BF16_COPY = 1
+WT_MEM_DEVICE = 0
+WT_MEM_PINNED_HOST = 1
+WT_DST_ZERO_COPY = 0
+WT_DST_STAGED = 1
+
+EXPORTS = [
+    "wt_plan_options_init", "wt_plan_check", "wt_plan_schedule", "wt_plan_create", "wt_prepare",
+    "wt_plan_get_info", "wt_plan_destroy", "wt_status_str", "wt_plan_last_error",
+    "wt_quantize_domain", "wt_cast_f32_range",
+]
+
+
+class wt_shard(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("rows", ctypes.c_int64)]
+
+
+class wt_task(ctypes.Structure):
+    _fields_ = [
+        ("shards", ctypes.POINTER(wt_shard)),
+        ("n_shards", ctypes.c_int32),
+        ("shard_mem", ctypes.c_int32),
+        ("cols", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("fusion_group", ctypes.c_int32),
+        ("dst_offset", ctypes.c_uint64),
+        ("scale_offset", ctypes.c_uint64),
+    ]
+
+
+class wt_plan_options(ctypes.Structure):
+    _fields_ = [
+        ("watermark_bytes", ctypes.c_uint64),
+        ("chunk_bytes", ctypes.c_uint64),
+        ("dst_write_mode", ctypes.c_int32),
+        ("device", ctypes.c_int32),
+        ("reserved", ctypes.c_uint32 * 6),
+    ]
+
+
+class wt_plan_info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "n_tasks", "n_outputs", "n_fp8_outputs", "n_copy_outputs", "n_tiles", "input_bytes", "output_bytes",
+        "n_launches", "n_chunks", "n_h2d_copies", "n_dst_copies", "staging_bytes")] + [("reserved", ctypes.c_int64 * 4)]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_ if n != "reserved"}
+
+
+class wt_sched_op(ctypes.Structure):
+    _fields_ = [
+        ("stage", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+        ("wait_chunk", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("bytes", ctypes.c_int64),
+        ("staging_offset", ctypes.c_int64),
+        ("staging_bytes", ctypes.c_int64),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libwt.so not found at {LIB_PATH}: build it first (python -m bf16_fp8_weight_amd.build or "
+            "__graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    P = ctypes.POINTER
+    L.wt_plan_options_init.restype = None
+    L.wt_plan_options_init.argtypes = [P(wt_plan_options)]
+    L.wt_plan_check.restype = ctypes.c_int
+    L.wt_plan_check.argtypes = [P(wt_task), sz, sz, i32, P(wt_plan_options), P(wt_plan_info)]
+    L.wt_plan_schedule.restype = ctypes.c_int
+    L.wt_plan_schedule.argtypes = [P(wt_task), sz, sz, i32, P(wt_plan_options), P(wt_sched_op), sz, P(sz)]
+    L.wt_plan_create.restype = ctypes.c_int
+    L.wt_plan_create.argtypes = [P(wt_task), sz, vp, sz, i32, P(wt_plan_options), P(vp)]
+    L.wt_prepare.restype = ctypes.c_int
+    L.wt_prepare.argtypes = [vp, vp]
+    L.wt_plan_get_info.restype = ctypes.c_int
+    L.wt_plan_get_info.argtypes = [vp, P(wt_plan_info)]
+    L.wt_plan_destroy.restype = None
+    L.wt_plan_destroy.argtypes = [vp]
+    L.wt_status_str.restype = ctypes.c_char_p
+    L.wt_status_str.argtypes = [ctypes.c_int]
+    L.wt_plan_last_error.restype = ctypes.c_char_p
+    L.wt_plan_last_error.argtypes = [vp]
+    L.wt_quantize_domain.restype = ctypes.c_int
+    L.wt_quantize_domain.argtypes = [vp, i64, i32, vp, vp]
+    L.wt_cast_f32_range.restype = ctypes.c_int
+    L.wt_cast_f32_range.argtypes = [ctypes.c_uint32, ctypes.c_uint64, vp, vp]
+    return L
+
+
+lib = _load()
+
+
+class WtError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        self.status = status
+        msg = lib.wt_status_str(status).decode()
+        super().__init__(msg + (f": {detail}" if detail else ""))
+
+
+def _check(st: int, plan=None) -> None:
+    if st != WT_OK:
+        d = lib.wt_plan_last_error(plan)
+        raise WtError(st, d.decode() if d else "")
+
+
+# ------------------------------------------------------------- same-name calls
+def wt_plan_options_init() -> wt_plan_options:
+    o = wt_plan_options()
+    lib.wt_plan_options_init(ctypes.byref(o))
+    return o
+
+
+class TaskTable:
+    """A ctypes task table plus the shard arrays it points to (kept alive)."""
+
+    def __init__(self, tasks: Sequence[dict]):
+        self._shards: List = []
+        self.arr = (wt_task * max(1, len(tasks)))()
+        self.n = len(tasks)
+        for i, t in enumerate(tasks):
+            sh = (wt_shard * max(1, len(t["shards"])))()
+            for k, (ptr, rows) in enumerate(t["shards"]):
+                sh[k].ptr = ptr or None
+                sh[k].rows = rows
+            self._shards.append(sh)
+            a = self.arr[i]
+            a.shards = ctypes.cast(sh, ctypes.POINTER(wt_shard)) if t["shards"] else None
+            a.n_shards = len(t["shards"])
+            a.shard_mem = t.get("shard_mem", WT_MEM_DEVICE)
+            a.cols = t["cols"]
+            a.dtype = t["dtype"]
+            a.fusion_group = t.get("fusion_group", -1)
+            a.dst_offset = t.get("dst_offset", 0)
+            a.scale_offset = t.get("scale_offset", 0)
+
+
+def wt_plan_check(table: TaskTable, dst_bytes: int, dst_kind: int = WT_MEM_DEVICE,
+                  opts: Optional[wt_plan_options] = None) -> dict:
+    info = wt_plan_info()
+    _check(lib.wt_plan_check(table.arr, table.n, dst_bytes, dst_kind, ctypes.byref(opts) if opts else None,
+                             ctypes.byref(info)))
+    return info.as_dict()
+
+
+def wt_plan_schedule(table: TaskTable, dst_bytes: int, dst_kind: int = WT_MEM_DEVICE,
+                     opts: Optional[wt_plan_options] = None) -> List[dict]:
+    n = ctypes.c_size_t(0)
+    po = ctypes.byref(opts) if opts else None
+    _check(lib.wt_plan_schedule(table.arr, table.n, dst_bytes, dst_kind, po, None, 0, ctypes.byref(n)))
+    ops = (wt_sched_op * max(1, n.value))()
+    _check(lib.wt_plan_schedule(table.arr, table.n, dst_bytes, dst_kind, po, ops, n.value, ctypes.byref(n)))
+    return [{f: int(getattr(ops[i], f)) for f, _ in wt_sched_op._fields_ if f != "reserved"} for i in range(n.value)]
+
+
+def wt_plan_create(table: TaskTable, dst_ptr: int, dst_bytes: int, dst_kind: int = WT_MEM_DEVICE,
+                   opts: Optional[wt_plan_options] = None) -> int:
+    out = ctypes.c_void_p(0)
+    _check(lib.wt_plan_create(table.arr, table.n, dst_ptr, dst_bytes, dst_kind,
+                              ctypes.byref(opts) if opts else None, ctypes.byref(out)))
+    return out.value
+
+
+def wt_prepare(plan: int, stream: int = 0) -> None:
+    _check(lib.wt_prepare(plan, stream or None), plan)
+
+
+def wt_plan_get_info(plan: int) -> dict:
+    info = wt_plan_info()
+    _check(lib.wt_plan_get_info(plan, ctypes.byref(info)), plan)
+    return info.as_dict()
+
+
+def wt_plan_destroy(plan: int) -> None:
+    lib.wt_plan_destroy(plan)
+
+
+def wt_status_str(status: int) -> str:
+    return lib.wt_status_str(status).decode()
+
+
+def wt_plan_last_error(plan: Optional[int] = None) -> str:
+    r = lib.wt_plan_last_error(plan)
+    return r.decode() if r else ""
+
+
+def wt_quantize_domain(amax_bits_ptr: int, n_amax: int, path: int, out_ptr: int, stream: int = 0) -> None:
+    _check(lib.wt_quantize_domain(amax_bits_ptr, n_amax, path, out_ptr, stream or None))
+
+
+def wt_cast_f32_range(first: int, count: int, out_ptr: int, stream: int = 0) -> None:
+    _check(lib.wt_cast_f32_range(first, count, out_ptr, stream or None))
+
+
+# ------------------------------------------------------------- workload glue
+def task_table(wl, group_base: int = 0) -> TaskTable:
+    """Task table for a bf16_fp8_weight_amd.workloads.Workload: one task per
+    component, components of a fused output share a fusion group."""
+    from . import workloads as W
+
+    tasks = []
+    for oi, o in enumerate(wl.outputs):
+        fused = len(o.parts) > 1
+        for p in o.parts:
+            tasks.append({
+                "shards": [(s.data_ptr() if r else 0, r) for s, r in zip(p.shards, p.shard_rows)],
+                "shard_mem": WT_MEM_PINNED_HOST if wl.shard_mem == "host" else WT_MEM_DEVICE,
+                "cols": o.cols,
+                "dtype": WT_FP8_E4M3FN_B128 if o.kind == W.FP8 else WT_BF16_COPY,
+                "fusion_group": group_base + oi if fused else -1,
+                "dst_offset": o.dst_offset,
+                "scale_offset": o.scale_offset,
+            })
+    return TaskTable(tasks)
+
+
+class Plan:
+    """Owns a wt_plan handle for a workload and a destination tensor."""
+
+    def __init__(self, wl, dst, dst_kind: int = WT_MEM_DEVICE, opts: Optional[wt_plan_options] = None):
+        self.table = task_table(wl)
+        self.dst = dst
+        self.handle = wt_plan_create(self.table, dst.data_ptr(), dst.numel() * dst.element_size(), dst_kind, opts)
+
+    def prepare(self, stream: int = 0) -> None:
+        wt_prepare(self.handle, stream)
+
+    def info(self) -> dict:
+        return wt_plan_get_info(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            wt_plan_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,220 @@
+/*
+ * wt.h -- C ABI of the MI355X parameter-preparation library (libwt.so).
+ *
+ * The library implements the "parameter preparation" stage of an RL
+ * weight-transfer pipeline ("Weight transfer for RL post-training in under 2
+ * seconds", Perplexity, 2025; section "Task pipeline"): after a training step
+ * it takes FSDP dim-0 row shards of BF16 weights, rebuilds each full tensor
+ * (the full_tensor() step), fuses projections (e.g. q/k/v -> qkv,
+ * gate/up -> gate_up), quantizes to FP8 and writes the bytes into a
+ * registered destination region at offsets fixed ahead of time by the
+ * controller's static schedule (section "Static schedule": the schedule is
+ * computed once, each iteration replays it). The region stands in for the
+ * remote inference GPU's memory that a one-sided RDMA WRITE would fill
+ * (section "RDMA WRITE: one-sided transfers"); the destination side gets no
+ * notification.
+ *
+ * Numerics of an FP8 output (the page says only "quantize if needed"; this
+ * is the reading the library implements): OCP FP8 E4M3 ("e4m3fn", max 448,
+ * no infinity) with one fp32 scale per 128x128 tile of the fused tensor,
+ * s = amax / 448 (s = 1 for an all-zero tile), each element
+ * cast(fl32(x / s)) with IEEE-rounded fp32 division and round-to-nearest-even
+ * with saturation. FP8 bytes are row-major [R x C]; scales are row-major
+ * fp32 over the ceil(R/128) x ceil(C/128) tile grid. A WT_BF16_COPY output is
+ * the fused BF16 bytes, unchanged.
+ *
+ * Conventions: every entry point returns a wt_status (no C++ exception ever
+ * crosses the ABI). All pointers are plain host or device addresses; sizes
+ * are in bytes unless a field says rows/cols. "stream" arguments are
+ * hipStream_t values passed as void* (NULL = the null stream). Separate plans
+ * are independent and may be used from different threads.
+ */
+#ifndef WT_H
+#define WT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wt_status {
+  WT_OK = 0,
+  WT_E_INVAL = 1,     /* malformed task table or argument */
+  WT_E_RANGE = 2,     /* a data or scale range falls outside [0, dst_bytes) */
+  WT_E_OVERLAP = 3,   /* two destination ranges overlap */
+  WT_E_ALIGN = 4,     /* misaligned shard pointer, BF16 dst_offset or scale_offset */
+  WT_E_NOMEM = 5,     /* host or device allocation failed */
+  WT_E_HIP = 6,       /* HIP runtime error; text from wt_plan_last_error() */
+  WT_E_WATERMARK = 7, /* watermark below the staging need of one output */
+  WT_E_STATE = 8      /* wt_prepare already running on this plan */
+} wt_status;
+
+/* Output data type of a task (and of its fusion group). */
+enum { WT_FP8_E4M3FN_B128 = 0, WT_BF16_COPY = 1 };
+
+/* Where shards or the destination region live. */
+enum { WT_MEM_DEVICE = 0, WT_MEM_PINNED_HOST = 1 };
+
+/* How prepared bytes reach the destination region (emulated RDMA WRITE). */
+enum {
+  WT_DST_ZERO_COPY = 0, /* the kernels store straight into the region */
+  WT_DST_STAGED = 1     /* kernels store into device staging; a copy stage moves them */
+};
+
+/* One FSDP shard: `rows` consecutive rows (row length = the task's cols,
+ * BF16, row-major, rows contiguous). rows may be 0 (ptr is then ignored).
+ * ptr must be 2-byte aligned. */
+typedef struct wt_shard {
+  const void *ptr;
+  int64_t rows;
+} wt_shard;
+
+/* One task = one source parameter tensor ("Task pipeline": each parameter
+ * tensor transfer is a task), given as its shards in rank order. Its full
+ * tensor is the dim-0 concatenation of the shards.
+ *
+ * fusion_group: -1 = the task is an output of its own. Tasks that share an
+ * id >= 0 form ONE output, their full tensors concatenated along dim 0 in
+ * table order (projection fusion); they must share cols, dtype and
+ * shard_mem, and the output's dst_offset / scale_offset are taken from the
+ * group's first task (the others' offsets are ignored).
+ *
+ * dst_offset: byte offset of the output's data in the destination region
+ * (FP8: R*C bytes; BF16 copy: 2*R*C bytes, offset must be even).
+ * scale_offset: byte offset of the fp32 scale grid (FP8 only; multiple of 4).
+ * A 1-D tensor of n elements is described as rows = n, cols = 1. */
+typedef struct wt_task {
+  const wt_shard *shards;
+  int32_t n_shards;
+  int32_t shard_mem; /* WT_MEM_DEVICE or WT_MEM_PINNED_HOST */
+  int64_t cols;
+  int32_t dtype; /* WT_FP8_E4M3FN_B128 or WT_BF16_COPY */
+  int32_t fusion_group;
+  uint64_t dst_offset;
+  uint64_t scale_offset;
+} wt_task;
+
+/* Plan options; wt_plan_options_init() fills the defaults. */
+typedef struct wt_plan_options {
+  /* Upper bound on temporary device memory held by tasks in flight
+   * ("GPU memory usage control": a task starts only while in-flight
+   * temporary memory is under a configurable watermark). Used for staging
+   * of pinned-host shards and, in WT_DST_STAGED mode, of outputs.
+   * Default 256 MiB. */
+  uint64_t watermark_bytes;
+  /* Target bytes of one pipeline chunk (outputs moved through the stages
+   * together, one kernel launch each). Default: min(32 MiB, watermark/2). */
+  uint64_t chunk_bytes;
+  int32_t dst_write_mode; /* WT_DST_ZERO_COPY (default) or WT_DST_STAGED */
+  int32_t device;         /* HIP device ordinal; -1 (default) = current device */
+  uint32_t reserved[6];
+} wt_plan_options;
+
+/* Shape of a plan, filled by wt_plan_check / wt_plan_get_info. */
+typedef struct wt_plan_info {
+  int64_t n_tasks;
+  int64_t n_outputs;
+  int64_t n_fp8_outputs;
+  int64_t n_copy_outputs;
+  int64_t n_tiles;            /* 128x128 tiles over all FP8 outputs */
+  int64_t input_bytes;        /* BF16 bytes read */
+  int64_t output_bytes;       /* FP8 + scale + BF16 bytes written */
+  int64_t n_launches;         /* kernel launches per wt_prepare */
+  int64_t n_chunks;           /* pipeline chunks (0 when no stage needs staging) */
+  int64_t n_h2d_copies;       /* host-to-device copies per wt_prepare */
+  int64_t n_dst_copies;       /* staging-to-destination copies per wt_prepare */
+  int64_t staging_bytes;      /* device staging allocated (<= watermark) */
+  int64_t reserved[4];
+} wt_plan_info;
+
+/* One operation of the replayed schedule, as listed by wt_plan_schedule. */
+typedef struct wt_sched_op {
+  int32_t stage;        /* 0 = host-to-device copy, 1 = prepare launch, 2 = destination copy */
+  int32_t chunk;        /* chunk index (-1: the launch over device-resident outputs) */
+  int32_t wait_chunk;   /* stage 0: chunk whose release this op waits for (-1: none) */
+  int32_t reserved;
+  int64_t bytes;        /* bytes moved (stages 0, 2) or prepared input bytes (stage 1) */
+  int64_t staging_offset; /* start of the chunk's staging slot in the ring */
+  int64_t staging_bytes;  /* size of the chunk's staging slot */
+} wt_sched_op;
+
+typedef struct wt_plan wt_plan;
+
+/* Fills `opts` with the defaults. */
+void wt_plan_options_init(wt_plan_options *opts);
+
+/* Validates a task table exactly as wt_plan_create does and describes the
+ * plan it would build, without touching any GPU (host only). opts may be
+ * NULL (defaults). info may be NULL. */
+wt_status wt_plan_check(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, int32_t dst_kind,
+                        const wt_plan_options *opts, wt_plan_info *info);
+
+/* Lists the operations one wt_prepare would enqueue, in enqueue order, for
+ * the plan wt_plan_check would build (host only). Writes at most max_ops
+ * records to ops (may be NULL) and the total count to *n_ops. */
+wt_status wt_plan_schedule(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, int32_t dst_kind,
+                           const wt_plan_options *opts, wt_sched_op *ops, size_t max_ops, size_t *n_ops);
+
+/* Builds a plan (the static schedule, computed once): validates the table,
+ * builds the device descriptor tables (outputs, row segments, tile and copy
+ * work lists), allocates staging within the watermark and creates the
+ * plan's streams and events. The table is copied; the caller may free it on
+ * return. Shard memory and the destination region stay owned by the caller
+ * and must outlive the plan; their ADDRESSES are fixed in the plan, their
+ * CONTENTS may change between wt_prepare calls.
+ * dst: destination region base (device pointer, or pinned host pointer when
+ * dst_kind is WT_MEM_PINNED_HOST), dst_bytes long. On failure *out is NULL. */
+wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
+                         const wt_plan_options *opts, wt_plan **out);
+
+/* Replays the plan: enqueues the whole preparation so that it is ordered
+ * after prior work on `stream` and completes before later work on `stream`.
+ * With device-resident shards and WT_DST_ZERO_COPY this is one kernel launch
+ * on `stream`. Pinned-host shards or WT_DST_STAGED run the three-stage
+ * pipeline (host-to-device copy, prepare, destination copy) on the plan's own
+ * streams, one in-order queue per stage, and join `stream` at the end.
+ * Returns without waiting for the GPU. No validation or allocation happens
+ * here. Returns WT_E_STATE if another wt_prepare on the same plan is running
+ * in another thread, WT_E_HIP on a runtime error. */
+wt_status wt_prepare(wt_plan *plan, void *stream);
+
+/* Copies the plan's shape into *info. */
+wt_status wt_plan_get_info(const wt_plan *plan, wt_plan_info *info);
+
+/* Waits for the plan's streams, then frees everything the plan owns (device
+ * tables, staging, streams, events). Never frees shards or the destination
+ * region. NULL is ignored. */
+void wt_plan_destroy(wt_plan *plan);
+
+/* Static text for a status code. */
+const char *wt_status_str(int status);
+
+/* Text of the last error recorded on `plan`, or, for plan == NULL, of the
+ * last failed wt_plan_create / wt_plan_check on the calling thread. */
+const char *wt_plan_last_error(const wt_plan *plan);
+
+/* ---- Element-function checks (exhaustive verification of the kernels' arithmetic) ----
+ * These run the same device code the prepare kernel runs per tile and per
+ * element, over complete input domains, so that the result can be compared
+ * with an independent implementation. */
+
+/* out[i * 65536 + x] = E4M3 byte that the prepare kernel writes for the BF16
+ * pattern x in a tile whose amax is the BF16 pattern amax_bits[i] (the sign
+ * bit of amax_bits is ignored; scale and division chosen exactly as in the
+ * prepare kernel). path = 0: the element function of the aligned (fast) tile
+ * path; path = 1: that of the general (any shape, any alignment) tile path.
+ * amax_bits and out are device pointers; out holds n_amax * 65536 bytes;
+ * 0 <= n_amax <= 2^20 (WT_E_INVAL otherwise). */
+wt_status wt_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, int32_t path, uint8_t *out, void *stream);
+
+/* out[i] = the kernel's fp32 -> E4M3 cast of the fp32 bit pattern first + i
+ * (wrapping modulo 2^32), for i < count. out is a device pointer. */
+wt_status wt_cast_f32_range(uint32_t first, uint64_t count, uint8_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WT_H */

@@ -1,0 +1,114 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, bit for
+bit, on the five workloads and on edge cases. Marked gpu."""
+import numpy as np
+import pytest
+import torch
+
+from bf16_fp8_weight_amd import workloads as W
+from gpu_util import Timer, assert_images_equal, log, oracle_image_threaded, run_library
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from bf16_fp8_weight_amd import wt  # noqa: F401  (fails loudly if libwt.so is missing)
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _parity(wl, **kw):
+    log(f"  workload {wl.name}: {len(wl.outputs)} outputs, {wl.input_bytes / 1e6:.1f} MB in, seed {wl.seed}")
+    with Timer("gpu"):
+        got, info = run_library(wl, **kw)
+    with Timer("oracle"):
+        want = oracle_image_threaded(wl)
+    assert_images_equal(got, want, wl)
+    return info
+
+
+def test_dense_layer_h1024():
+    wl = W.dense_layer_h1024(device="cuda")
+    info = _parity(wl)
+    assert info["n_launches"] == 1
+
+
+def test_ragged_stress_reduced():
+    wl = W.ragged_stress(device="cuda", n_tensors=40, max_dim=1400)
+    _parity(wl)
+
+
+@pytest.mark.parametrize("shapes,n_shards,align", [
+    ([(1, 1), (1, 129), (129, 1), (128, 128), (129, 129), (3000, 1)], 3, 256),
+    ([(1, 8), (8, 8), (127, 136), (300, 264), (1000, 24)], 8, 256),   # aligned fast path, tiny/edge tiles
+    ([(200, 160), (64, 64), (129, 17)], 300, 256),                    # many empty shards
+    ([(257, 512), (100, 4096)], 1, 1),                                 # unaligned destination offsets
+])
+def test_edge_shapes(shapes, n_shards, align):
+    wl = W.custom(shapes, n_shards=n_shards, device="cuda", align=align, dist="t")
+    _parity(wl)
+
+
+def test_fused_components_straddling_tiles():
+    wl = W.custom([(100, 256), (90, 256), (200, 256)], n_shards=3, device="cuda", fused=True)
+    _parity(wl)
+
+
+def test_single_row_shards():
+    wl = W.custom([(130, 1024)], n_shards=130, device="cuda", fused=False)
+    _parity(wl)
+
+
+def test_task_order_independent():
+    from bf16_fp8_weight_amd import wt
+    wl = W.custom([(300, 512), (64, 64), (1, 300), (129, 17), (256, 1024)], n_shards=3, device="cuda")
+    ref, _ = run_library(wl)
+    tab = wt.task_table(wl)
+    tasks = [tab.arr[i] for i in range(tab.n)]
+    perm = [3, 0, 4, 2, 1]
+    shuffled = wt.TaskTable([])
+    arr = (wt.wt_task * len(perm))()
+    for j, i in enumerate(perm):
+        arr[j] = tasks[i]
+    shuffled.arr, shuffled.n, shuffled._shards = arr, len(perm), tab._shards
+    got, _ = run_library(wl, table=shuffled)
+    assert np.array_equal(got, ref)
+
+
+def test_new_contents_same_plan():
+    # the plan fixes addresses; contents change every step
+    from bf16_fp8_weight_amd import wt
+    wl = W.custom([(384, 1024), (256, 256)], n_shards=4, device="cuda")
+    dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    tab = wt.task_table(wl)
+    h = wt.wt_plan_create(tab, dst.data_ptr(), wl.dst_bytes)
+    try:
+        for step in range(3):
+            g = torch.Generator(device="cuda").manual_seed(100 + step)
+            for o in wl.outputs:
+                for p in o.parts:
+                    for s in p.shards:
+                        s.copy_((torch.randn(s.shape, generator=g, device="cuda") * (0.01 * (step + 1))).to(torch.bfloat16))
+            wt.wt_prepare(h, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            want = oracle_image_threaded(wl)
+            assert_images_equal(dst.cpu().numpy(), want, wl)
+    finally:
+        wt.wt_plan_destroy(h)
+
+
+def test_dense_7b_full():
+    wl = W.dense_7b(device="cuda")
+    _parity(wl)
+
+
+def test_kimi_k2_moe_full():
+    wl = W.kimi_k2_expert_share(device="cuda")
+    _parity(wl)
+
+
+def test_ragged_stress_full():
+    wl = W.ragged_stress(device="cuda")
+    _parity(wl)

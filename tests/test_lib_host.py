@@ -1,0 +1,182 @@
+"""libwt.so on the CPU: it loads, exports every call include/wt.h declares,
+and its host-only plan logic (validation, plan shape, pipeline schedule)
+behaves as documented. No GPU call is made here."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from bf16_fp8_weight_amd import workloads as W
+from fake_tables import fake_table
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def wt():
+    from bf16_fp8_weight_amd import wt as _wt
+    return _wt
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "wt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wt_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_match_header(wt):
+    names = _declared()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(wt.lib, n), n
+    assert set(names) == set(wt.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", wt.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in names:
+        assert n in syms, n
+
+
+def test_status_strings(wt):
+    assert wt.wt_status_str(0) == "WT_OK"
+    for s in range(1, 9):
+        assert wt.wt_status_str(s).startswith("WT_E_")
+
+
+def test_options_defaults(wt):
+    o = wt.wt_plan_options_init()
+    assert o.watermark_bytes == 256 << 20 and o.dst_write_mode == wt.WT_DST_ZERO_COPY and o.device == -1
+
+
+def _one(wt, **kw):
+    t = {"shards": [(0x10000, 4)], "shard_mem": wt.WT_MEM_DEVICE, "cols": 128,
+         "dtype": wt.WT_FP8_E4M3FN_B128, "fusion_group": -1, "dst_offset": 0, "scale_offset": 512}
+    t.update(kw)
+    return t
+
+
+def _status(wt, tasks, dst_bytes=4096, kind=None, opts=None):
+    tab = wt.TaskTable(tasks)
+    try:
+        wt.wt_plan_check(tab, dst_bytes, wt.WT_MEM_DEVICE if kind is None else kind, opts)
+        return 0
+    except wt.WtError as e:
+        return e.status
+
+
+def test_validation_errors(wt):
+    E = wt
+    assert _status(wt, [_one(wt)]) == 0
+    assert _status(wt, []) == E.WT_E_INVAL
+    assert _status(wt, [_one(wt, shards=[(0, 4)])]) == E.WT_E_INVAL            # NULL shard with rows
+    assert _status(wt, [_one(wt, shards=[(0x10001, 4)])]) == E.WT_E_ALIGN      # odd BF16 pointer
+    assert _status(wt, [_one(wt, shards=[(0x10000, -1)])]) == E.WT_E_INVAL     # negative rows
+    assert _status(wt, [_one(wt, shards=[(0, 0)])]) == E.WT_E_INVAL            # no rows at all
+    assert _status(wt, [_one(wt, cols=0)]) == E.WT_E_INVAL
+    assert _status(wt, [_one(wt, dtype=7)]) == E.WT_E_INVAL
+    assert _status(wt, [_one(wt, shard_mem=5)]) == E.WT_E_INVAL
+    assert _status(wt, [_one(wt, dst_offset=4000)]) == E.WT_E_RANGE            # 512 data bytes past 4096
+    assert _status(wt, [_one(wt, scale_offset=4094)]) == E.WT_E_ALIGN
+    assert _status(wt, [_one(wt, scale_offset=4096)]) == E.WT_E_RANGE
+    assert _status(wt, [_one(wt, scale_offset=100)]) == E.WT_E_OVERLAP         # scale inside the data
+    assert _status(wt, [_one(wt), _one(wt, dst_offset=256, scale_offset=1024)]) == E.WT_E_OVERLAP
+    assert _status(wt, [_one(wt, dtype=wt.WT_BF16_COPY, dst_offset=1)]) == E.WT_E_ALIGN
+    # fusion group members must agree on cols / dtype / memory
+    assert _status(wt, [_one(wt, fusion_group=3), _one(wt, fusion_group=3, cols=64)]) == E.WT_E_INVAL
+    assert _status(wt, [_one(wt, fusion_group=3), _one(wt, fusion_group=3, shard_mem=wt.WT_MEM_PINNED_HOST)]) == E.WT_E_INVAL
+    assert _status(wt, [_one(wt, fusion_group=-2)]) == E.WT_E_INVAL
+    assert _status(wt, [_one(wt)], kind=9) == E.WT_E_INVAL
+    # pinned-host shards need staging: a watermark below one output's need fails
+    o = wt.wt_plan_options_init()
+    o.watermark_bytes = 1024
+    assert _status(wt, [_one(wt, shard_mem=wt.WT_MEM_PINNED_HOST)], opts=o) == E.WT_E_WATERMARK
+    assert "watermark" in wt.wt_plan_last_error(None)
+
+
+def test_fused_group_offsets_from_first_task(wt):
+    # the second member's offsets are ignored, so they may be anything
+    ok = [_one(wt, fusion_group=1, scale_offset=1024), _one(wt, fusion_group=1, dst_offset=10 ** 9, scale_offset=10 ** 9)]
+    info = wt.wt_plan_check(wt.TaskTable(ok), 4096)
+    assert info["n_outputs"] == 1 and info["n_tiles"] == 1
+
+
+@pytest.mark.parametrize("make", [W.dense_layer_h1024, W.kimi_k2_expert_share, W.dense_7b])
+def test_plan_shape_matches_workload(wt, make):
+    wl = make(materialize=False)
+    info = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
+    assert info["n_outputs"] == len(wl.outputs)
+    assert info["n_tiles"] == wl.n_tiles
+    assert info["input_bytes"] == wl.input_bytes
+    assert info["output_bytes"] == wl.output_bytes
+    assert info["n_chunks"] == 0 and info["staging_bytes"] == 0
+    assert info["n_launches"] == 1  # one batched launch over the whole table
+
+
+def test_ragged_shapes_use_the_general_kernel(wt):
+    wl = W.ragged_stress(materialize=False, n_tensors=64)
+    info = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
+    assert info["n_tiles"] == wl.n_tiles
+    assert info["n_launches"] == 2  # aligned outputs + general outputs
+
+
+def _check_schedule(ops, watermark, stages):
+    # FIFO per stage: each stage's ops run chunks in increasing order
+    for st in stages:
+        seq = [o["chunk"] for o in ops if o["stage"] == st and o["chunk"] >= 0]
+        assert seq == sorted(seq) and len(seq) == len(set(seq))
+    # worst case (nothing completes unless a wait forces it): at each
+    # admission the live chunks' slots are disjoint and within the watermark
+    first = {}
+    for o in ops:
+        first.setdefault(o["chunk"], o)
+    released = -1
+    slots = {}
+    for c in sorted(k for k in first if k >= 0):
+        o = first[c]
+        if o["wait_chunk"] >= 0:
+            assert o["wait_chunk"] < c
+            released = max(released, o["wait_chunk"])
+        slots[c] = (o["staging_offset"], o["staging_offset"] + o["staging_bytes"])
+        live = [slots[k] for k in slots if released < k <= c]
+        assert sum(b - a for a, b in live) <= watermark
+        assert all(b <= watermark for _, b in live)
+        live.sort()
+        for (a0, b0), (a1, b1) in zip(live, live[1:]):
+            assert b0 <= a1, "live staging slots overlap"
+
+
+@pytest.mark.parametrize("watermark_mb", [160, 256, 1024])
+def test_pipeline_schedule_host_shards(wt, watermark_mb):
+    wl = W.mla_many_small(materialize=False)
+    o = wt.wt_plan_options_init()
+    o.watermark_bytes = watermark_mb << 20
+    tab = fake_table(wt, wl, align=16)
+    info = wt.wt_plan_check(tab, wl.dst_bytes, opts=o)
+    ops = wt.wt_plan_schedule(tab, wl.dst_bytes, opts=o)
+    assert info["n_chunks"] == max(op["chunk"] for op in ops) + 1
+    assert info["staging_bytes"] <= o.watermark_bytes
+    assert sum(op["bytes"] for op in ops if op["stage"] == 0) == wl.input_bytes
+    assert sum(op["bytes"] for op in ops if op["stage"] == 1) == wl.input_bytes
+    _check_schedule(ops, o.watermark_bytes, stages=(0, 1))
+    # contiguous host shards merge into one copy per chunk
+    assert info["n_h2d_copies"] == info["n_chunks"]
+
+
+def test_pipeline_schedule_staged_mode(wt):
+    wl = W.dense_layer_h1024(materialize=False)
+    o = wt.wt_plan_options_init()
+    o.dst_write_mode = wt.WT_DST_STAGED
+    o.watermark_bytes = 16 << 20
+    tab = fake_table(wt, wl)
+    ops = wt.wt_plan_schedule(tab, wl.dst_bytes, opts=o)
+    assert [op["stage"] for op in ops] == [1, 2] * (len(ops) // 2)
+    assert sum(op["bytes"] for op in ops if op["stage"] == 2) == wl.output_bytes
+    _check_schedule(ops, o.watermark_bytes, stages=(1, 2))
+
+
+def test_gapped_host_shards_copy_per_run(wt):
+    wl = W.custom([(300, 256), (64, 128)], n_shards=4, device="cpu")
+    o = wt.wt_plan_options_init()
+    tab = fake_table(wt, wl, gap=512, host=True)
+    info = wt.wt_plan_check(tab, wl.dst_bytes, opts=o)
+    assert info["n_h2d_copies"] == 8  # no merging across gaps
