@@ -37,6 +37,8 @@ def main() -> int:
     ap.add_argument("--workload", default="kimi_k2_moe",
                     choices=["kimi_k2_moe", "dense_7b", "dense_layer_h1024", "ragged_stress"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="instead of the workload, time a plain device-to-device copy of BYTES (counter calibration)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = min(16, cores))")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters for the current kernel")
@@ -52,6 +54,8 @@ def main() -> int:
     from bf16_fp8_weight_amd import wt
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        return _copy_calibration(args.calibrate_copy, args.steps, args.warmup)
     make = W.WORKLOADS[args.workload]
     t0 = time.time()
     wl = make(device="cuda")
@@ -117,7 +121,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16->fp8e4m3fn (fp32 scale math)",
+        "dtype": "f32",
         "data": "synthetic: seeded N(0, 0.02) BF16, random weights of the stated shapes",
         "config": {
             "workload": wl.name,
@@ -146,6 +150,27 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     plan.close()
     return 0 if verified in (None, True) else 1
+
+
+def _copy_calibration(nbytes: int, steps: int, warmup: int) -> int:
+    """Plain copy of nbytes (reads nbytes, writes nbytes) on the current stream."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / steps
+    print(json.dumps({"metric": "copy_calibration", "bytes_copied": nbytes, "ms_per_copy": round(t * 1e3, 5),
+                      "GBps_read_plus_write": round(2 * nbytes / t / 1e9, 1)}), flush=True)
+    return 0
 
 
 def _kernel_sha() -> str:

@@ -28,30 +28,38 @@ COMMON = [
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False, save_temps_dir: str | None = None) -> str:
-    """Compiles every source and links libwt.so. Always rebuilds."""
-    objdir = os.path.join(ROOT, "_build")
+def build(verbose: bool = False, save_temps_dir: str | None = None, defines=(), out: str | None = None) -> str:
+    """Compiles every source and links libwt.so (or `out`). Always rebuilds.
+    `defines` are extra -D options (kernel tuning knobs)."""
+    objdir = os.path.join(ROOT, "_build", "default" if not defines else "_".join(d.replace("=", "") for d in defines))
     os.makedirs(objdir, exist_ok=True)
     objs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(objdir, src + ".o")
-        cmd = [HIPCC, *COMMON, *DEVICE, "-c", path, "-o", obj]
+        cmd = [HIPCC, *COMMON, *DEVICE, *("-D" + d for d in defines), "-c", path, "-o", obj]
         if save_temps_dir and src.endswith(".hip"):
             cmd += ["-save-temps=obj"]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True, cwd=save_temps_dir or objdir)
         objs.append(obj)
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    target = out or LIB_PATH
+    tmp = target + ".tmp%d" % os.getpid()
     link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB_PATH)
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("-D", action="append", default=[], help="extra define, e.g. -D WT_SAT_CLAMP=0")
+    ap.add_argument("-o", default=None, help="output library path")
+    a = ap.parse_args()
+    print(build(verbose=a.v, defines=a.D, out=a.o))

@@ -354,7 +354,7 @@ void build_tables(const Layout &L, const std::vector<int32_t> &outputs, const Ba
     d.rows = H.rows;
     d.cols = (int32_t)H.cols;
     d.tiles_c = (int32_t)H.tiles_c;
-    bool fast = (H.cols % 8 == 0) && (d.q % 8 == 0);
+    bool fast = (H.cols % 8 == 0) && (H.cols < (1 << 24)) && (d.q % 8 == 0);
     for (size_t s = 0; s < H.segs.size(); ++s) {
       DevSeg g{};
       g.src = addr.seg_src((int32_t)k, o, (int32_t)s);
@@ -365,18 +365,34 @@ void build_tables(const Layout &L, const std::vector<int32_t> &outputs, const Ba
     }
     d.flags = fast ? kOutFast : 0;
     t->outs.push_back(d);
-    std::vector<TileItem> &dstv = fast ? t->fast : t->general;
     size_t s = 0;
     for (int64_t I = 0; I < H.tiles_r; ++I) {
       while (s + 1 < H.segs.size() && H.segs[s].row0 + H.segs[s].nrows <= I * kTile) ++s;
-      for (int64_t J = 0; J < H.tiles_c; ++J)
-        dstv.push_back(TileItem{out_idx, (uint32_t)I, (uint32_t)J, seg_base + (uint32_t)s});
+      const bool full_rows = (I + 1) * kTile <= H.rows;
+      const bool one_seg = H.segs[s].row0 + H.segs[s].nrows >= std::min<int64_t>((I + 1) * kTile, H.rows);
+      for (int64_t J = 0; J < H.tiles_c; ++J) {
+        const bool full = full_rows && (J + 1) * kTile <= H.cols;
+        const TileItem item{out_idx, (uint32_t)I, (uint32_t)J, seg_base + (uint32_t)s};
+        if (!fast) {
+          t->general.push_back(item);
+        } else if (!(full && one_seg)) {
+          t->edge.push_back(item);
+        } else {
+          const DevSeg &g = t->segs[seg_base + s];
+          RegDesc r{};
+          r.src = g.src + 2 * ((uint64_t)(I * kTile - g.row0) * (uint64_t)H.cols + (uint64_t)(J * kTile));
+          r.q = d.q + (uint64_t)(I * kTile) * (uint64_t)H.cols + (uint64_t)(J * kTile);
+          r.s = d.s + 4 * ((uint64_t)I * (uint64_t)H.tiles_c + (uint64_t)J);
+          r.C = (uint32_t)H.cols;
+          t->fast.push_back(r);
+        }
+      }
     }
   }
 }
 
 int launches_for(const HostTables &t) {
-  return ((t.fast.size() + t.copies.size()) > 0 ? 1 : 0) + (t.general.empty() ? 0 : 1);
+  return ((t.fast.size() + t.edge.size() + t.copies.size()) > 0 ? 1 : 0) + (t.general.empty() ? 0 : 1);
 }
 
 void schedule_ops(const Layout &L, std::vector<wt_sched_op> *ops) {

@@ -77,7 +77,8 @@ wt_status build_layout(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, i
 struct HostTables {
   std::vector<DevOut> outs;
   std::vector<DevSeg> segs;
-  std::vector<TileItem> fast, general;
+  std::vector<RegDesc> fast;
+  std::vector<TileItem> edge, general;
   std::vector<CopyItem> copies;
 };
 
@@ -92,7 +93,7 @@ struct BatchAddr {
 
 void build_tables(const Layout &L, const std::vector<int32_t> &outputs, const BatchAddr &addr, HostTables *t);
 
-// Number of kernel launches a batch needs (fast+copy kernel, general kernel).
+// Number of kernel launches a batch needs (aligned tiles + copies, general tiles).
 int launches_for(const HostTables &t);
 
 // Splits one byte-range copy into CopyItems (alignment-aware, <= kCopyItemMax bytes each).

@@ -5,7 +5,7 @@
 // rows straight from the shard buffers through the row-segment table, so no
 // full tensor is ever materialised. Per 128 x 128 tile of an FP8 output:
 // amax of |x|, s = amax / 448 (1 for an all-zero tile), q = fl32(x / s) with
-// IEEE division, then E4M3 (OCP "e4m3fn") round-to-nearest-even with
+// IEEE-rounded division, then E4M3 (OCP "e4m3fn") round-to-nearest-even with
 // saturation, stored row-major with the fp32 scale at its grid position.
 // BF16 pass-through outputs are byte copies. The path is HBM-bound: every
 // input byte is read once and every output byte written once.
@@ -14,6 +14,46 @@
 #include "wt_internal.h"
 
 namespace wt {
+
+// ------------------------------------------------------------ memory access
+// Descriptor tables are read-only for the kernel's lifetime and read at
+// workgroup-uniform addresses: constant address space, so they become scalar
+// loads. Tensor data goes through the global address space (global_load /
+// global_store rather than flat instructions, which would also count against
+// the LDS counter).
+template <class T>
+using cptr = const __attribute__((address_space(4))) T *;
+template <class T>
+using gptr = __attribute__((address_space(1))) T *;
+template <class T>
+using gcptr = const __attribute__((address_space(1))) T *;
+
+// p[i] from a descriptor table (scalar load when i is uniform).
+template <class T>
+__device__ __forceinline__ T ld_table(const T *p, uint64_t i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return ((cptr<T>)(uintptr_t)p)[i];
+#else
+  return p[i];
+#endif
+}
+// Global-memory load / store at a byte address.
+template <class T>
+__device__ __forceinline__ T ld_global(uint64_t a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(gcptr<T>)(uintptr_t)a;
+#else
+  return *(const T *)(uintptr_t)a;
+#endif
+}
+template <class T>
+__device__ __forceinline__ void st_global(uint64_t a, const T &v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  *(gptr<T>)(uintptr_t)a = v;
+#else
+  *(T *)(uintptr_t)a = v;
+#endif
+}
 
 // ------------------------------------------------------------ element math
 
@@ -38,99 +78,292 @@ __device__ __forceinline__ float tile_scale(uint32_t amax16) {
   return __uint_as_float(amax16 << 16) / 448.0f;
 }
 
-// Saturation to the E4M3 range before the hardware convert; together with
-// round-to-nearest-even in v_cvt_pk_fp8_f32 this gives the saturating cast.
+// Division x / s for one tile. For tiles with s >= 2^-100 the quotient is
+// computed from the tile's correctly rounded reciprocal r = 1/s with one
+// exact residual (Markstein's correction, Handbook of Floating-Point
+// Arithmetic, section on division with FMA): y = x*r, d = y*s - x (exact in
+// one FMA), q = y - d*r. The residual is arranged as y*s - x (not x - y*s)
+// so that signed zeros come out as IEEE division gives them. Below the
+// threshold (amax < about 448 * 2^-100) intermediate products can be
+// subnormal and the tile uses the compiler's IEEE division. Which form is
+// used is one uniform decision per tile; the complete (x, amax) domain of
+// BF16 is checked against IEEE division by wt_quantize_domain.
+#ifndef WT_RECIP_DIV
+#define WT_RECIP_DIV 1
+#endif
+
+struct TileQ {
+  float s;  // the tile's scale
+  float r;  // fl(1 / s), used when recip
+  bool recip;
+};
+
+__device__ __forceinline__ TileQ tile_quant(uint32_t amax16) {
+  TileQ t;
+  t.s = tile_scale(amax16);
+  t.r = 1.0f / t.s;
+  // uniform across the workgroup: every thread holds the same amax16
+  t.recip = WT_RECIP_DIV && __builtin_amdgcn_readfirstlane(__float_as_uint(t.s) >= 0x0D800000u);  // s >= 2^-100
+  return t;
+}
+
+template <bool Recip>
+__device__ __forceinline__ float qdiv(float x, const TileQ &t) {
+  if (Recip) {
+    const float y = x * t.r;
+    const float d = __builtin_fmaf(y, t.s, -x);
+    return __builtin_fmaf(-d, t.r, y);
+  }
+  return x / t.s;
+}
+
+// Saturation to [-448, 448] before the hardware convert (v_cvt_pk_fp8_f32
+// rounds to nearest even but does not saturate, and takes no clamp modifier).
+// On this path every quotient is at most 448.88 in magnitude, below 464, so
+// the clamp never changes a byte; it keeps the cast saturating by
+// construction.
 __device__ __forceinline__ float sat448(float q) { return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f); }
 
 // Four BF16 (two packed words) -> four E4M3 bytes, little-endian in one word.
-__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float s) {
-  const float a = bf16_lo(w0) / s, b = bf16_hi(w0) / s;
-  const float c = bf16_lo(w1) / s, d = bf16_hi(w1) / s;
-  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+template <bool Recip>
+__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const TileQ &t) {
+  const float a = qdiv<Recip>(bf16_lo(w0), t), b = qdiv<Recip>(bf16_hi(w0), t);
+  const float c = qdiv<Recip>(bf16_lo(w1), t), d = qdiv<Recip>(bf16_hi(w1), t);
+  // the first convert fills bytes 0-1 and keeps bytes 2-3 of its third
+  // operand, which the second convert then overwrites: any register will do
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), (int)w1, false);
   r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), (int)r, true);
   return r;
 }
 
 // One BF16 -> one E4M3 byte (same arithmetic as quant4, one lane).
-__device__ __forceinline__ uint32_t quant1(uint32_t xbits, float s) {
-  const float a = __uint_as_float(xbits << 16) / s;
+template <bool Recip>
+__device__ __forceinline__ uint32_t quant1(uint32_t xbits, const TileQ &t) {
+  const float a = qdiv<Recip>(__uint_as_float(xbits << 16), t);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), 0.0f, 0, false) & 0xFFu;
 }
 
-// Max over the workgroup (4 waves). red: 4 words of LDS.
+// Max over a workgroup of NW waves. Within a wave: DPP row shifts leave the
+// max of each 16-lane row in its lane 15; the four row maxima are read out
+// with v_readlane. Across waves: one LDS word per wave. red: NW words of LDS.
+template <int NW>
 __device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t *red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  // row_shr:n = 0x110 + n; lanes shifted in from outside the row read 0 (bound_ctrl)
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, true));
+  const uint32_t w = max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 15), (uint32_t)__builtin_amdgcn_readlane((int)m, 31)),
+                         max((uint32_t)__builtin_amdgcn_readlane((int)m, 47), (uint32_t)__builtin_amdgcn_readlane((int)m, 63)));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
   __syncthreads();
-  return max(max(red[0], red[1]), max(red[2], red[3]));
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = max(r, red[i]);
+  return r;
 }
 
-// ------------------------------------------------------------ tile: fast path
-// cols % 8 == 0, 16-byte aligned rows, 8-byte aligned FP8 rows. Thread t
-// owns 8 columns (16 bytes of BF16) of rows (t >> 4) + 16 k, k = 0..7: a
-// wave reads four full 256-byte tile rows per instruction and writes four
-// 128-byte FP8 rows per store. The 64 values stay in registers between the
-// amax and the quantization.
-__device__ __forceinline__ void fast_tile(const LaunchTables &T, const TileItem it, uint32_t *red) {
-  const DevOut o = T.outs[it.out];
-  const int tid = threadIdx.x;
-  const int cc = tid & 15;
-  const int rr = tid >> 4;
-  const int64_t r0 = (int64_t)it.tile_row * kTile;
-  const int64_t rlim = min(r0 + (int64_t)kTile, o.rows);
-  const int64_t c = (int64_t)it.tile_col * kTile + cc * 8;
-  const bool col_ok = c < o.cols;
-  const int64_t C = o.cols;
+// ------------------------------------------------------------ aligned tiles
+// Outputs with cols % 8 == 0 (and < 2^24), 16-byte aligned rows and 8-byte
+// aligned FP8 rows. A tile is 128 rows x 16 chunks of 8 columns (16 bytes of
+// BF16 each). A workgroup of TT threads takes one tile; thread t owns chunks
+// t + TT k (k < CH = 2048 / TT): row (t + TT k) / 16, chunk t % 16. Each
+// wave instruction reads four complete 256-byte tile rows and each FP8 store
+// writes four complete 128-byte rows.
+//
+// Load pacing. Measured on MI355X (8.5 GB streams of this 2:1 read:write
+// shape), delivered HBM bandwidth peaks when each compute unit keeps about
+// 24 KB of loads in flight, and falls by 10% or more with either 16 KB or
+// 36 KB and up: with every load of a tile issued at once, a fully occupied
+// compute unit keeps over 100 KB in flight and the stream tops out near
+// 5.4 TB/s. So each wave keeps WT_LOADS_IN_FLIGHT loads in flight (it waits
+// for one before issuing the next), and the dynamic-LDS request admits at
+// most WT_BLOCKS_PER_CU workgroups per compute unit: 3 workgroups x 8 waves
+// x one 1 KB load = 24 KB. The arithmetic of one workgroup runs while the
+// others' loads are in flight.
+#ifndef WT_TILE_THREADS
+#define WT_TILE_THREADS 512
+#endif
+#ifndef WT_LOADS_IN_FLIGHT
+#define WT_LOADS_IN_FLIGHT 1
+#endif
+#ifndef WT_BLOCKS_PER_CU
+#define WT_BLOCKS_PER_CU 3
+#endif
+constexpr int TT = WT_TILE_THREADS;
+constexpr int CH = 2048 / TT;
+constexpr int TW = TT / 64;
+static_assert(TT == 256 || TT == 512 || TT == 1024, "tile block size");
+static_assert(WT_LOADS_IN_FLIGHT == 1 || WT_LOADS_IN_FLIGHT == 2, "loads in flight per wave");
 
-  uint4 v[8];
-  uint32_t idx = it.seg;
-  DevSeg g = T.segs[idx];
-  const bool single = g.row_end >= rlim;  // uniform: one shard serves the whole tile row
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int64_t r = r0 + rr + 16 * k;
-    v[k] = make_uint4(0, 0, 0, 0);
-    if (col_ok && r < rlim) {
-      if (!single)
-        while (r >= g.row_end) g = T.segs[++idx];
-      const uint4 *p = reinterpret_cast<const uint4 *>(g.src + (uint64_t)(((r - g.row0) * C + c) * 2));
-      v[k] = *p;
-    }
-  }
+// Paces this wave's loads: after issuing chunk k, wait until at most
+// WT_LOADS_IN_FLIGHT - 1 of its vector memory operations are outstanding.
+// Pacing only: the compiler's own waits still guard every use of a loaded
+// register.
+__device__ __forceinline__ void pace_loads(int k) {
+  if (WT_LOADS_IN_FLIGHT == 1 || (k & 1)) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
+__device__ __forceinline__ uint32_t amax_chunks(const uint4 (&v)[CH]) {
   uint32_t m = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < CH; ++k) {
     m = pk_max_u16(m, abs2(v[k].x));
     m = pk_max_u16(m, abs2(v[k].y));
     m = pk_max_u16(m, abs2(v[k].z));
     m = pk_max_u16(m, abs2(v[k].w));
   }
-  m = max(m & 0xFFFFu, m >> 16);
-  const uint32_t amax16 = block_max(m, red);
-  const float s = tile_scale(amax16);
-
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int64_t r = r0 + rr + 16 * k;
-    if (col_ok && r < rlim) {
-      uint2 q;
-      q.x = quant4(v[k].x, v[k].y, s);
-      q.y = quant4(v[k].z, v[k].w, s);
-      *reinterpret_cast<uint2 *>(o.q + (uint64_t)(r * C + c)) = q;
-    }
-  }
-  if (tid == 0) reinterpret_cast<float *>(o.s)[(uint64_t)it.tile_row * (uint64_t)o.tiles_c + it.tile_col] = s;
+  return max(m & 0xFFFFu, m >> 16);
 }
 
-// ------------------------------------------------------------ tile: general path
-// Any cols and alignment. Thread t owns column t & 127 of rows (t >> 7) + 2 k.
-// Pass 1 reads the tile for its amax, pass 2 reads it again (now from cache)
-// and quantizes; 2-byte loads and 1-byte stores, coalesced along each row.
+// Element offset of this thread's chunk k inside a tile of row length C.
+__device__ __forceinline__ uint32_t chunk_off(int k, uint32_t C) {
+  const uint32_t c = threadIdx.x + TT * k;
+  return (c >> 4) * C + (c & 15) * 8;
+}
+
+// Regular tile: a full 128 x 128 tile whose rows all come from one shard,
+// addresses resolved at plan time (one scalar load of its descriptor); every
+// chunk is loaded and stored unconditionally.
+__device__ __forceinline__ void reg_tile(const LaunchTables &T, uint32_t b, uint32_t *red) {
+  const RegDesc x = ld_table(T.fast_tiles, b);
+  uint4 v[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    v[k] = ld_global<uint4>(x.src + 2 * chunk_off(k, x.C));
+    pace_loads(k);
+  }
+  const TileQ t = tile_quant(block_max<TW>(amax_chunks(v), red));
+  if (t.recip) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      uint2 q;
+      q.x = quant4<true>(v[k].x, v[k].y, t);
+      q.y = quant4<true>(v[k].z, v[k].w, t);
+      st_global<uint2>(x.q + chunk_off(k, x.C), q);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      uint2 q;
+      q.x = quant4<false>(v[k].x, v[k].y, t);
+      q.y = quant4<false>(v[k].z, v[k].w, t);
+      st_global<uint2>(x.q + chunk_off(k, x.C), q);
+    }
+  }
+  if (threadIdx.x == 0) st_global<float>(x.s, t.s);
+}
+
+// Edge tile: partial (last tile row or column of an output), or rows from
+// several shards. Chunks past the tensor's last row read the tile's last row,
+// chunks past its last column read the tile's first columns: values of the
+// same tile, which leave the amax unchanged, and are never stored. The
+// window's segments are walked with scalar loads.
+template <bool Recip>
+__device__ __forceinline__ void edge_store(const uint4 (&v)[CH], uint64_t qbase, uint32_t C, uint32_t valid,
+                                           const TileQ &t) {
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    if (valid & (1u << k)) {
+      uint2 q;
+      q.x = quant4<Recip>(v[k].x, v[k].y, t);
+      q.y = quant4<Recip>(v[k].z, v[k].w, t);
+      st_global<uint2>(qbase + chunk_off(k, C), q);
+    }
+  }
+}
+
+__device__ __forceinline__ void edge_tile(const LaunchTables &T, uint32_t b, uint32_t *red) {
+  const TileItem it = ld_table(T.edge_tiles, b);
+  const DevOut o = ld_table(T.outs, it.out);
+  const uint32_t C = (uint32_t)o.cols;
+  const int64_t r0 = (int64_t)it.tile_row * kTile;
+  const uint32_t nr = (uint32_t)min((int64_t)kTile, o.rows - r0);  // rows in this tile
+  const uint32_t c0 = it.tile_col * kTile;
+
+  uint32_t valid = 0;
+  uint32_t row[CH], col[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const uint32_t c = threadIdx.x + TT * k;
+    const uint32_t lr = c >> 4, cl = (c & 15) * 8;
+    if (lr < nr && c0 + cl < C) valid |= 1u << k;
+    row[k] = min(lr, nr - 1);
+    col[k] = c0 + cl < C ? cl : 0;
+  }
+  uint64_t src[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) src[k] = 0;
+  uint32_t si = it.seg;
+  DevSeg g = ld_table(T.segs, si);
+  for (;;) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int64_t r = r0 + row[k];
+      if (r >= g.row0 && r < g.row_end) src[k] = g.src + 2 * ((uint64_t)(r - g.row0) * C + c0 + col[k]);
+    }
+    if (g.row_end >= r0 + nr) break;
+    g = ld_table(T.segs, ++si);
+  }
+  uint4 v[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    v[k] = ld_global<uint4>(src[k]);
+    pace_loads(k);
+  }
+
+  const TileQ t = tile_quant(block_max<TW>(amax_chunks(v), red));
+  const uint64_t qbase = o.q + (uint64_t)r0 * C + c0;
+  if (t.recip)
+    edge_store<true>(v, qbase, C, valid, t);
+  else
+    edge_store<false>(v, qbase, C, valid, t);
+  if (threadIdx.x == 0) st_global<float>(o.s + 4 * ((uint64_t)it.tile_row * (uint64_t)o.tiles_c + it.tile_col), t.s);
+}
+
+// ------------------------------------------------------------ pass-through copy
+// One wave per item; src, dst and bytes are multiples of width.
+__device__ __forceinline__ void copy_item(const CopyItem ci, int lane) {
+  switch (ci.width) {
+    case 16:
+      for (uint32_t i = lane; i < ci.bytes / 16; i += 64) st_global(ci.dst + 16ull * i, ld_global<uint4>(ci.src + 16ull * i));
+      break;
+    case 4:
+      for (uint32_t i = lane; i < ci.bytes / 4; i += 64) st_global(ci.dst + 4ull * i, ld_global<uint32_t>(ci.src + 4ull * i));
+      break;
+    case 2:
+      for (uint32_t i = lane; i < ci.bytes / 2; i += 64) st_global(ci.dst + 2ull * i, ld_global<uint16_t>(ci.src + 2ull * i));
+      break;
+    default:
+      for (uint32_t i = lane; i < ci.bytes; i += 64) st_global(ci.dst + i, ld_global<uint8_t>(ci.src + i));
+      break;
+  }
+}
+
+// ------------------------------------------------------------ general tiles
+// Any cols and alignment (256 threads). Thread t owns column t & 127 of rows
+// (t >> 7) + 2 k. Pass 1 reads the tile for its amax, pass 2 reads it again
+// (from cache) and quantizes; 2-byte loads and 1-byte stores, coalesced
+// along each row.
+constexpr int GT = 256;
+
+template <bool Recip>
+__device__ __forceinline__ void general_store(const LaunchTables &T, const TileItem &it, const DevOut &o, int64_t r0,
+                                              int64_t rlim, int64_t c, bool col_ok, int rb, const TileQ &t) {
+  const int64_t C = o.cols;
+  uint32_t idx = it.seg;
+  DevSeg g = T.segs[idx];
+  for (int k = 0; k < kTile / 2; ++k) {
+    const int64_t r = r0 + rb + 2 * k;
+    if (!col_ok || r >= rlim) break;
+    while (r >= g.row_end) g = T.segs[++idx];
+    const uint16_t x = ld_global<uint16_t>(g.src + (uint64_t)(((r - g.row0) * C + c) * 2));
+    st_global<uint8_t>(o.q + (uint64_t)(r * C + c), (uint8_t)quant1<Recip>(x, t));
+  }
+}
+
 __device__ __forceinline__ void general_tile(const LaunchTables &T, const TileItem it, uint32_t *red) {
-  const DevOut o = T.outs[it.out];
+  const DevOut o = ld_table(T.outs, it.out);
   const int tid = threadIdx.x;
   const int64_t r0 = (int64_t)it.tile_row * kTile;
   const int64_t rlim = min(r0 + (int64_t)kTile, o.rows);
@@ -147,104 +380,75 @@ __device__ __forceinline__ void general_tile(const LaunchTables &T, const TileIt
       const int64_t r = r0 + rb + 2 * k;
       if (!col_ok || r >= rlim) break;
       while (r >= g.row_end) g = T.segs[++idx];
-      const uint16_t x = *reinterpret_cast<const uint16_t *>(g.src + (uint64_t)(((r - g.row0) * C + c) * 2));
+      const uint16_t x = ld_global<uint16_t>(g.src + (uint64_t)(((r - g.row0) * C + c) * 2));
       m = max(m, (uint32_t)(x & 0x7FFFu));
     }
   }
-  const uint32_t amax16 = block_max(m, red);
-  const float s = tile_scale(amax16);
-  {
-    uint32_t idx = it.seg;
-    DevSeg g = T.segs[idx];
-    for (int k = 0; k < kTile / 2; ++k) {
-      const int64_t r = r0 + rb + 2 * k;
-      if (!col_ok || r >= rlim) break;
-      while (r >= g.row_end) g = T.segs[++idx];
-      const uint16_t x = *reinterpret_cast<const uint16_t *>(g.src + (uint64_t)(((r - g.row0) * C + c) * 2));
-      *reinterpret_cast<uint8_t *>(o.q + (uint64_t)(r * C + c)) = (uint8_t)quant1(x, s);
-    }
-  }
-  if (tid == 0) reinterpret_cast<float *>(o.s)[(uint64_t)it.tile_row * (uint64_t)o.tiles_c + it.tile_col] = s;
-}
-
-// ------------------------------------------------------------ pass-through copy
-// One wave per item; src, dst and bytes are multiples of width.
-__device__ __forceinline__ void copy_item(const CopyItem ci, int lane) {
-  switch (ci.width) {
-    case 16: {
-      const uint4 *s = reinterpret_cast<const uint4 *>(ci.src);
-      uint4 *d = reinterpret_cast<uint4 *>(ci.dst);
-      for (uint32_t i = lane; i < ci.bytes / 16; i += 64) d[i] = s[i];
-      break;
-    }
-    case 4: {
-      const uint32_t *s = reinterpret_cast<const uint32_t *>(ci.src);
-      uint32_t *d = reinterpret_cast<uint32_t *>(ci.dst);
-      for (uint32_t i = lane; i < ci.bytes / 4; i += 64) d[i] = s[i];
-      break;
-    }
-    case 2: {
-      const uint16_t *s = reinterpret_cast<const uint16_t *>(ci.src);
-      uint16_t *d = reinterpret_cast<uint16_t *>(ci.dst);
-      for (uint32_t i = lane; i < ci.bytes / 2; i += 64) d[i] = s[i];
-      break;
-    }
-    default: {
-      const uint8_t *s = reinterpret_cast<const uint8_t *>(ci.src);
-      uint8_t *d = reinterpret_cast<uint8_t *>(ci.dst);
-      for (uint32_t i = lane; i < ci.bytes; i += 64) d[i] = s[i];
-      break;
-    }
-  }
+  const TileQ t = tile_quant(block_max<GT / 64>(m, red));
+  if (t.recip)
+    general_store<true>(T, it, o, r0, rlim, c, col_ok, rb, t);
+  else
+    general_store<false>(T, it, o, r0, rlim, c, col_ok, rb, t);
+  if (tid == 0) st_global<float>(o.s + 4 * ((uint64_t)it.tile_row * (uint64_t)o.tiles_c + it.tile_col), t.s);
 }
 
 // ------------------------------------------------------------ kernels
 
-// Blocks [0, n_fast): one fast tile each; then kCopiesPerBlock copy items per block.
-__global__ __launch_bounds__(kBlock) void prep_fast_copy_kernel(LaunchTables T) {
-  __shared__ uint32_t red[4];
-  const uint32_t b = blockIdx.x;
+// Blocks [0, n_fast): one regular tile each; [n_fast, n_fast + n_edge): one
+// edge tile each; then TW copy items per block (one per wave). At most
+// WT_BLOCKS_PER_CU blocks per compute unit (dynamic-LDS request).
+__global__ __launch_bounds__(TT) void prep_fast_copy_kernel(LaunchTables T) {
+  __shared__ uint32_t red[TW];
+  uint32_t b = blockIdx.x;
   if (b < T.n_fast) {
-    fast_tile(T, T.fast_tiles[b], red);
+    reg_tile(T, b, red);
     return;
   }
-  const uint32_t ci = (b - T.n_fast) * kCopiesPerBlock + (threadIdx.x >> 6);
-  if (ci < T.n_copies) copy_item(T.copies[ci], threadIdx.x & 63);
+  b -= T.n_fast;
+  if (b < T.n_edge) {
+    edge_tile(T, b, red);
+    return;
+  }
+  b -= T.n_edge;
+  const uint32_t ci = b * TW + (threadIdx.x >> 6);
+  if (ci < T.n_copies) copy_item(ld_table(T.copies, ci), threadIdx.x & 63);
 }
 
-__global__ __launch_bounds__(kBlock) void prep_general_kernel(LaunchTables T) {
-  __shared__ uint32_t red[4];
-  general_tile(T, T.general_tiles[blockIdx.x], red);
+__global__ __launch_bounds__(GT) void prep_general_kernel(LaunchTables T) {
+  __shared__ uint32_t red[GT / 64];
+  general_tile(T, ld_table(T.general_tiles, blockIdx.x), red);
 }
 
-// Element-function check: out[i * 65536 + x] for every BF16 x, four per thread,
-// through the same tile_scale / quant4 as the fast tile path.
-__global__ __launch_bounds__(kBlock) void quantize_domain_kernel(const uint16_t *amax_bits, int64_t n_amax,
-                                                                 uint8_t *out) {
-  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+// Element-function check: out[i * 65536 + x] for every BF16 x, four per
+// thread, through the same tile_quant / quant4 as the aligned tile paths.
+__global__ __launch_bounds__(256) void quantize_domain_kernel(const uint16_t *amax_bits, int64_t n_amax,
+                                                              uint8_t *out) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t i = gid >> 14;
   if (i >= n_amax) return;
   const uint32_t x0 = (uint32_t)(gid & 16383) * 4;
-  const float s = tile_scale(amax_bits[i] & 0x7FFFu);
+  // one amax per 16384 threads: uniform within each wave
+  const TileQ t = tile_quant(amax_bits[i] & 0x7FFFu);
   const uint32_t w0 = x0 | ((x0 + 1) << 16);
   const uint32_t w1 = (x0 + 2) | ((x0 + 3) << 16);
-  *reinterpret_cast<uint32_t *>(out + i * 65536 + x0) = quant4(w0, w1, s);
+  *reinterpret_cast<uint32_t *>(out + i * 65536 + x0) = t.recip ? quant4<true>(w0, w1, t) : quant4<false>(w0, w1, t);
 }
 
 // The same domain through quant1 (the general tile path's element function).
-__global__ __launch_bounds__(kBlock) void quantize_domain1_kernel(const uint16_t *amax_bits, int64_t n_amax,
-                                                                  uint8_t *out) {
-  const int64_t gid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+__global__ __launch_bounds__(256) void quantize_domain1_kernel(const uint16_t *amax_bits, int64_t n_amax,
+                                                               uint8_t *out) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t i = gid >> 16;
   if (i >= n_amax) return;
   const uint32_t x = (uint32_t)(gid & 65535);
-  const float s = tile_scale(amax_bits[i] & 0x7FFFu);
-  out[i * 65536 + x] = (uint8_t)quant1(x, s);
+  const TileQ t = tile_quant(amax_bits[i] & 0x7FFFu);
+  out[i * 65536 + x] = (uint8_t)(t.recip ? quant1<true>(x, t) : quant1<false>(x, t));
 }
 
-// Cast check: the saturating E4M3 cast of fp32 patterns first + i.
-__global__ __launch_bounds__(kBlock) void cast_range_kernel(uint32_t first, uint64_t count, uint8_t *out) {
-  const uint64_t i = ((uint64_t)blockIdx.x * kBlock + threadIdx.x) * 4;
+// Cast check: the hardware round-to-nearest-even E4M3 convert of fp32
+// patterns first + i, after the clamp to [-448, 448] (the saturating cast).
+__global__ __launch_bounds__(256) void cast_range_kernel(uint32_t first, uint64_t count, uint8_t *out) {
+  const uint64_t i = ((uint64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= count) return;
   float f[4];
 #pragma unroll
@@ -260,16 +464,34 @@ __global__ __launch_bounds__(kBlock) void cast_range_kernel(uint32_t first, uint
 
 // ------------------------------------------------------------ launchers
 
+// Dynamic-LDS request that admits at most WT_BLOCKS_PER_CU workgroups of
+// prep_fast_copy_kernel per compute unit of the current device (0 when the
+// device's per-block limit does not allow the cap).
+static uint32_t pacing_lds() {
+  int dev = 0, lds_cu = 0, lds_blk = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds_cu <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const uint32_t lds = (uint32_t)lds_cu / (WT_BLOCKS_PER_CU + 1) + 1;
+  const uint32_t static_lds = 4 * TW;
+  return lds + static_lds <= (uint32_t)lds_blk ? lds : 0;
+}
+
 hipError_t launch_batch(const LaunchTables &T, hipStream_t stream) {
-  const uint64_t copy_blocks = (T.n_copies + kCopiesPerBlock - 1) / kCopiesPerBlock;
-  const uint64_t blocks = (uint64_t)T.n_fast + copy_blocks;
+  const uint64_t copy_blocks = (T.n_copies + TW - 1) / TW;
+  const uint64_t blocks = (uint64_t)T.n_fast + T.n_edge + copy_blocks;
   if (blocks > 0) {
-    hipLaunchKernelGGL(prep_fast_copy_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, stream, T);
+    if (blocks > UINT32_MAX / TT) return hipErrorInvalidValue;
+    static const uint32_t lds = pacing_lds();
+    hipLaunchKernelGGL(prep_fast_copy_kernel, dim3((uint32_t)blocks), dim3(TT), lds, stream, T);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (T.n_general > 0) {
-    hipLaunchKernelGGL(prep_general_kernel, dim3(T.n_general), dim3(kBlock), 0, stream, T);
+    hipLaunchKernelGGL(prep_general_kernel, dim3(T.n_general), dim3(GT), 0, stream, T);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -280,13 +502,11 @@ hipError_t launch_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, uin
                                   hipStream_t stream) {
   if (n_amax <= 0) return hipSuccess;
   if (variant == 0) {
-    const uint64_t blocks = (uint64_t)n_amax * 16384 / kBlock;
-    hipLaunchKernelGGL(quantize_domain_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, stream, amax_bits, n_amax,
-                       out);
+    const uint64_t blocks = (uint64_t)n_amax * 16384 / 256;
+    hipLaunchKernelGGL(quantize_domain_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, amax_bits, n_amax, out);
   } else {
-    const uint64_t blocks = (uint64_t)n_amax * 65536 / kBlock;
-    hipLaunchKernelGGL(quantize_domain1_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, stream, amax_bits, n_amax,
-                       out);
+    const uint64_t blocks = (uint64_t)n_amax * 65536 / 256;
+    hipLaunchKernelGGL(quantize_domain1_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, amax_bits, n_amax, out);
   }
   return hipGetLastError();
 }
@@ -294,8 +514,8 @@ hipError_t launch_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, uin
 hipError_t launch_cast_range(uint32_t first, uint64_t count, uint8_t *out, hipStream_t stream) {
   if (count == 0) return hipSuccess;
   const uint64_t threads = (count + 3) / 4;
-  const uint64_t blocks = (threads + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(cast_range_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, stream, first, count, out);
+  const uint64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL(cast_range_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, first, count, out);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@
 // Everything is enqueued asynchronously; the host never polls.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstring>
@@ -234,10 +235,11 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
   }
   size_t total = 0;
   for (const HostTables &t : hts)
-    total += blob_bytes(t.outs) + blob_bytes(t.segs) + blob_bytes(t.fast) + blob_bytes(t.general) +
-             blob_bytes(t.copies);
-  std::vector<uint8_t> blob(std::max<size_t>(total, 256), 0);
-  if (total > 0) HIP_OR(p, hipMalloc((void **)&p->tables, total));
+    total += blob_bytes(t.outs) + blob_bytes(t.segs) + blob_bytes(t.fast) + blob_bytes(t.edge) +
+             blob_bytes(t.general) + blob_bytes(t.copies);
+  total = std::max<size_t>(total, 256);
+  std::vector<uint8_t> blob(total, 0);
+  HIP_OR(p, hipMalloc((void **)&p->tables, total));
   size_t off = 0;
   for (const HostTables &t : hts) {
     LaunchTables T{};
@@ -250,19 +252,22 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
     };
     T.outs = (const DevOut *)(uintptr_t)put(t.outs);
     T.segs = (const DevSeg *)(uintptr_t)put(t.segs);
-    T.fast_tiles = (const TileItem *)(uintptr_t)put(t.fast);
+    T.fast_tiles = (const RegDesc *)(uintptr_t)put(t.fast);
+    T.edge_tiles = (const TileItem *)(uintptr_t)put(t.edge);
     T.general_tiles = (const TileItem *)(uintptr_t)put(t.general);
     T.copies = (const CopyItem *)(uintptr_t)put(t.copies);
-    if (t.fast.size() > UINT32_MAX / 2 || t.general.size() > UINT32_MAX / 2 || t.copies.size() > UINT32_MAX / 2) {
+    if (t.fast.size() > UINT32_MAX / 2 || t.edge.size() > UINT32_MAX / 2 || t.general.size() > UINT32_MAX / 2 ||
+        t.copies.size() > UINT32_MAX / 2) {
       set_err(p, "work list too large for one launch");
       return WT_E_INVAL;
     }
     T.n_fast = (uint32_t)t.fast.size();
+    T.n_edge = (uint32_t)t.edge.size();
     T.n_general = (uint32_t)t.general.size();
     T.n_copies = (uint32_t)t.copies.size();
     p->batches.push_back(T);
   }
-  if (total > 0) HIP_OR(p, hipMemcpy(p->tables, blob.data(), total, hipMemcpyHostToDevice));
+  HIP_OR(p, hipMemcpy(p->tables, blob.data(), total, hipMemcpyHostToDevice));
 
   if (p->pipeline) {
     HIP_OR(p, hipStreamCreateWithFlags(&p->s_h2d, hipStreamNonBlocking));

@@ -7,13 +7,11 @@
 namespace wt {
 
 constexpr int kTile = 128;            // FP8 scale tile edge (128 x 128 elements)
-constexpr int kBlock = 256;           // threads per workgroup (4 wave64)
 constexpr uint32_t kCopyItemMax = 16384;  // bytes per copy work item (one wave each)
-constexpr int kCopiesPerBlock = kBlock / 64;
 
 // Output flags.
 enum : int32_t {
-  kOutFast = 1,  // cols % 8 == 0, data base 8-byte aligned, every segment 16-byte aligned
+  kOutFast = 1,  // cols % 8 == 0, cols < 2^24, data base 8-byte aligned, every segment 16-byte aligned
 };
 
 // One FP8 output tensor of a launch.
@@ -49,6 +47,17 @@ struct TileItem {
 };
 static_assert(sizeof(TileItem) == 16, "TileItem layout");
 
+// One regular tile (full 128 x 128, rows from one shard, aligned output),
+// with every address resolved at plan time: one scalar load per tile.
+struct RegDesc {
+  uint64_t src;  // BF16 address of the tile's element (0, 0)
+  uint64_t q;    // FP8 address of the tile's element (0, 0)
+  uint64_t s;    // address of the tile's scale
+  uint32_t C;    // row length in elements (< 2^24)
+  uint32_t pad;
+};
+static_assert(sizeof(RegDesc) == 32, "RegDesc layout");
+
 // One byte-range copy (BF16 pass-through). width = 16, 4 or 2: src, dst and
 // bytes are all multiples of width.
 struct CopyItem {
@@ -64,13 +73,14 @@ static_assert(sizeof(CopyItem) == 32, "CopyItem layout");
 struct LaunchTables {
   const DevOut *outs;
   const DevSeg *segs;
-  const TileItem *fast_tiles;     // tiles of kOutFast outputs
+  const RegDesc *fast_tiles;      // regular tiles of kOutFast outputs: full, rows from one shard
+  const TileItem *edge_tiles;     // other tiles of kOutFast outputs: partial, or rows from several shards
   const TileItem *general_tiles;  // tiles of the other outputs
   const CopyItem *copies;
   uint32_t n_fast;
+  uint32_t n_edge;
   uint32_t n_general;
   uint32_t n_copies;
-  uint32_t pad;
 };
 
 }  // namespace wt

@@ -12,7 +12,8 @@ import os
 from typing import List, Optional, Sequence
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libwt.so")
+# WT_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("WT_LIB") or os.path.join(PKG, "libwt.so")
 
 WT_OK = 0
 WT_E_INVAL, WT_E_RANGE, WT_E_OVERLAP, WT_E_ALIGN, WT_E_NOMEM, WT_E_HIP, WT_E_WATERMARK, WT_E_STATE = range(1, 9)
