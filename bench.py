@@ -35,7 +35,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="kimi_k2_moe",
-                    choices=["kimi_k2_moe", "dense_7b", "dense_layer_h1024", "ragged_stress"])
+                    choices=["kimi_k2_moe", "dense_7b", "dense_layer_h1024", "ragged_stress", "mla_many_small",
+                             "mla_many_small_device"])
+    ap.add_argument("--dst-mode", default="zero-copy", choices=["zero-copy", "staged"],
+                    help="how prepared bytes reach the destination region")
+    ap.add_argument("--dst-kind", default="device", choices=["device", "pinned"],
+                    help="destination region in device memory or pinned host memory")
+    ap.add_argument("--watermark-mb", type=int, default=0, help="pipeline watermark (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the workload, time a plain device-to-device copy of BYTES (counter calibration)")
@@ -56,15 +62,26 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         return _copy_calibration(args.calibrate_copy, args.steps, args.warmup)
-    make = W.WORKLOADS[args.workload]
     t0 = time.time()
-    wl = make(device="cuda")
+    if args.workload == "mla_many_small_device":
+        wl = W.mla_many_small(device="cuda", host=False)
+    else:
+        wl = W.WORKLOADS[args.workload](device="cuda")
     torch.cuda.synchronize()
     log(f"workload {wl.name}: {len(wl.outputs)} outputs, {wl.input_bytes / 1e9:.3f} GB BF16 in, "
         f"{wl.n_tiles} tiles, generated in {time.time() - t0:.1f}s")
 
-    dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
-    plan = wt.Plan(wl, dst)
+    if args.dst_kind == "device":
+        dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+        dst_kind = wt.WT_MEM_DEVICE
+    else:
+        dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8).pin_memory()
+        dst_kind = wt.WT_MEM_PINNED_HOST
+    opts = wt.wt_plan_options_init()
+    opts.dst_write_mode = wt.WT_DST_STAGED if args.dst_mode == "staged" else wt.WT_DST_ZERO_COPY
+    if args.watermark_mb:
+        opts.watermark_bytes = args.watermark_mb << 20
+    plan = wt.Plan(wl, dst, dst_kind, opts)
     info = plan.info()
     log(f"plan: {info}")
     stream = torch.cuda.current_stream()
@@ -95,6 +112,10 @@ def main() -> int:
     log(f"steps {args.steps}: {ms_per_step:.4f} ms/step wall, launch avg {avg_launch_s * 1e3:.4f} ms "
         f"(min {min(launch_ms):.4f}, max {max(launch_ms):.4f}); prepared {value:.1f} GB/s; "
         f"HBM {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.3f} of peak")
+
+    pipeline = None
+    if wl.shard_mem == "host":
+        pipeline = _h2d_ceiling(wl, ms_per_step, args.steps)
 
     traffic = None
     try:
@@ -130,7 +151,7 @@ def main() -> int:
             "output_bytes": wl.output_bytes,
             "tiles": wl.n_tiles,
             "shards_per_tensor": 8,
-            "dst_mode": "zero-copy, device-resident shards",
+            "dst_mode": f"{args.dst_mode}, {args.dst_kind} destination, {wl.shard_mem}-resident shards",
         },
         "pct_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
         "roofline": {
@@ -147,9 +168,37 @@ def main() -> int:
         "cpu_baseline": cpu,
         "verified_vs_oracle": verified,
     }
+    if pipeline is not None:
+        line["pipeline"] = pipeline
     print(json.dumps(line), flush=True)
     plan.close()
     return 0 if verified in (None, True) else 1
+
+
+def _h2d_ceiling(wl, ms_per_step: float, steps: int) -> dict:
+    """Times a bare host-to-device copy of the workload's pinned shard arena
+    (the same bytes the pipeline's first stage moves) and relates it to the
+    pipeline's time per step."""
+    import torch
+
+    arena = wl.arena
+    dev = torch.empty(arena.numel(), dtype=torch.uint8, device="cuda")
+    dev.copy_(arena, non_blocking=True)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(3, min(steps, 10))
+    s.record()
+    for _ in range(n):
+        dev.copy_(arena, non_blocking=True)
+    e.record()
+    torch.cuda.synchronize()
+    t_h2d = s.elapsed_time(e) / n
+    out = {"h2d_ms": round(t_h2d, 4), "h2d_GBps": round(arena.numel() / t_h2d / 1e6, 2),
+           "pipeline_ms": round(ms_per_step, 4), "overlap_eff": round(t_h2d / ms_per_step, 4),
+           "arena_bytes": int(arena.numel())}
+    log(f"pipeline: bare H2D of the {arena.numel() / 1e9:.3f} GB arena {t_h2d:.3f} ms "
+        f"({out['h2d_GBps']} GB/s); pipeline {ms_per_step:.3f} ms; overlap efficiency {out['overlap_eff']}")
+    return out
 
 
 def _copy_calibration(nbytes: int, steps: int, warmup: int) -> int:

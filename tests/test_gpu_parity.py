@@ -112,3 +112,33 @@ def test_kimi_k2_moe_full():
 def test_ragged_stress_full():
     wl = W.ragged_stress(device="cuda")
     _parity(wl)
+
+
+def _scaled_workload(shapes, scales, seed, n_shards=2):
+    """custom() workload whose tensors are multiplied by per-tensor scales (in
+    fp32, then rounded to BF16) to reach extreme magnitudes."""
+    wl = W.custom(shapes, n_shards=n_shards, device="cuda", seed=seed)
+    for o, sc in zip(wl.outputs, scales):
+        for p in o.parts:
+            for sh in p.shards:
+                sh.copy_((sh.to(torch.float32) * sc).to(torch.bfloat16))
+    return wl
+
+
+def test_extreme_magnitudes():
+    # tiny tiles take the kernel's IEEE-division branch (s < 2^-100), BF16
+    # subnormals included; huge tiles approach the BF16 maximum
+    shapes = [(256, 256), (128, 384), (300, 136), (130, 1000), (256, 128)]
+    scales = [1e-30, 1e-36, 3e-39, 1e34, 1e-25]
+    _parity(_scaled_workload(shapes, scales, seed=31))
+
+
+def test_row_wider_than_fast_path_limit():
+    # 2^24 + 8 columns: beyond the aligned path's 32-bit tile offsets, so the
+    # general path takes it
+    _parity(W.custom([(2, (1 << 24) + 8)], n_shards=2, device="cuda", seed=32))
+
+
+def test_single_large_tensor():
+    # one 4 GiB tensor in 8 shards
+    _parity(W.custom([(131072, 16384)], n_shards=8, device="cuda", seed=33))
