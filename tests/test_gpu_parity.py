@@ -140,5 +140,5 @@ def test_row_wider_than_fast_path_limit():
 
 
 def test_single_large_tensor():
-    # one 4 GiB tensor in 8 shards
-    _parity(W.custom([(131072, 16384)], n_shards=8, device="cuda", seed=33))
+    # one 2 GiB tensor (2^30 elements) in 8 shards
+    _parity(W.custom([(65536, 16384)], n_shards=8, device="cuda", seed=33))
