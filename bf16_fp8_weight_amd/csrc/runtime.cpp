@@ -70,6 +70,14 @@ void set_err(wt_plan *p, const std::string &m) {
   }
 }
 
+}  // namespace
+
+namespace wt {
+void set_thread_error(const std::string &msg) { g_last_error = msg; }
+}  // namespace wt
+
+namespace {
+
 std::string hip_msg(const char *what, hipError_t e) {
   return std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
 }

@@ -145,6 +145,26 @@ def pack(outputs: List[OutputSpec], align: int = 256, start: int = 0) -> int:
     return align_up(off, max(align, 1))
 
 
+def metadata(wl: "Workload", with_ptrs: bool = True):
+    """The metadata the controller collects for a workload: training
+    parameters (name, shape, number of FSDP shards, where they live) and
+    inference tensors (name, the training parameters fused into it, dtype).
+    A training parameter is named "<inference tensor>/<component>"."""
+    params, dsts = [], []
+    for o in wl.outputs:
+        comps = []
+        for p in o.parts:
+            nm = f"{o.name}/{p.name}"
+            d = {"name": nm, "rows": p.rows, "cols": o.cols, "n_shards": len(p.shard_rows),
+                 "shard_mem": 1 if wl.shard_mem == "host" else 0}
+            if with_ptrs and p.shards:
+                d["shard_ptrs"] = [s.data_ptr() if r else 0 for s, r in zip(p.shards, p.shard_rows)]
+            params.append(d)
+            comps.append(nm)
+        dsts.append({"name": o.name, "components": comps, "dtype": 0 if o.kind == FP8 else 1})
+    return params, dsts
+
+
 # ---------------------------------------------------------------- generators
 def _gen(device: str, seed: int) -> torch.Generator:
     g = torch.Generator(device=device)

@@ -28,6 +28,7 @@ EXPORTS = [
     "wt_plan_options_init", "wt_plan_check", "wt_plan_schedule", "wt_plan_create", "wt_prepare",
     "wt_plan_get_info", "wt_plan_destroy", "wt_status_str", "wt_plan_last_error",
     "wt_quantize_domain", "wt_cast_f32_range",
+    "wt_schedule_build", "wt_schedule_info", "wt_schedule_output", "wt_schedule_tasks", "wt_schedule_destroy",
 ]
 
 
@@ -79,6 +80,30 @@ class wt_sched_op(ctypes.Structure):
     ]
 
 
+class wt_param_meta(ctypes.Structure):
+    _fields_ = [
+        ("name", ctypes.c_char_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("n_shards", ctypes.c_int32),
+        ("shard_mem", ctypes.c_int32),
+        ("shard_ptrs", ctypes.POINTER(ctypes.c_void_p)),
+    ]
+
+
+class wt_dst_meta(ctypes.Structure):
+    _fields_ = [
+        ("name", ctypes.c_char_p),
+        ("components", ctypes.POINTER(ctypes.c_char_p)),
+        ("n_components", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class wt_schedule_options(ctypes.Structure):
+    _fields_ = [("align", ctypes.c_uint64), ("n_sources", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -109,6 +134,16 @@ def _load() -> ctypes.CDLL:
     L.wt_quantize_domain.argtypes = [vp, i64, i32, vp, vp]
     L.wt_cast_f32_range.restype = ctypes.c_int
     L.wt_cast_f32_range.argtypes = [ctypes.c_uint32, ctypes.c_uint64, vp, vp]
+    L.wt_schedule_build.restype = ctypes.c_int
+    L.wt_schedule_build.argtypes = [P(wt_param_meta), sz, P(wt_dst_meta), sz, P(wt_schedule_options), P(vp)]
+    L.wt_schedule_info.restype = ctypes.c_int
+    L.wt_schedule_info.argtypes = [vp, P(sz), P(sz), P(ctypes.c_uint64), P(sz)]
+    L.wt_schedule_output.restype = ctypes.c_int
+    L.wt_schedule_output.argtypes = [vp, sz, P(ctypes.c_uint64), P(ctypes.c_uint64), P(i32), P(ctypes.c_uint64)]
+    L.wt_schedule_tasks.restype = ctypes.c_int
+    L.wt_schedule_tasks.argtypes = [vp, i32, P(wt_task), sz, P(wt_shard), sz, P(sz), P(sz)]
+    L.wt_schedule_destroy.restype = None
+    L.wt_schedule_destroy.argtypes = [vp]
     return L
 
 
@@ -157,6 +192,18 @@ class TaskTable:
             a.fusion_group = t.get("fusion_group", -1)
             a.dst_offset = t.get("dst_offset", 0)
             a.scale_offset = t.get("scale_offset", 0)
+
+    def as_dicts(self) -> List[dict]:
+        """The table read back in the form the constructor takes."""
+        out = []
+        for i in range(self.n):
+            a = self.arr[i]
+            out.append({
+                "shards": [(a.shards[k].ptr or 0, a.shards[k].rows) for k in range(a.n_shards)],
+                "shard_mem": a.shard_mem, "cols": a.cols, "dtype": a.dtype, "fusion_group": a.fusion_group,
+                "dst_offset": a.dst_offset, "scale_offset": a.scale_offset,
+            })
+        return out
 
 
 def wt_plan_check(table: TaskTable, dst_bytes: int, dst_kind: int = WT_MEM_DEVICE,
@@ -214,6 +261,83 @@ def wt_quantize_domain(amax_bits_ptr: int, n_amax: int, path: int, out_ptr: int,
 
 def wt_cast_f32_range(first: int, count: int, out_ptr: int, stream: int = 0) -> None:
     _check(lib.wt_cast_f32_range(first, count, out_ptr, stream or None))
+
+
+# ------------------------------------------------------------- schedule builder
+class Schedule:
+    """Result of wt_schedule_build; the same calls as methods.
+
+    params: dicts {name, rows, cols, n_shards, shard_mem?, shard_ptrs?}
+    dsts:   dicts {name, components: [names], dtype}
+    """
+
+    def __init__(self, params, dsts, align: int = 256, n_sources: int = 1):
+        self._keep = []
+        pa = (wt_param_meta * max(1, len(params)))()
+        for i, p in enumerate(params):
+            nm = p["name"].encode()
+            self._keep.append(nm)
+            pa[i].name = nm
+            pa[i].rows, pa[i].cols = p["rows"], p["cols"]
+            pa[i].n_shards = p["n_shards"]
+            pa[i].shard_mem = p.get("shard_mem", WT_MEM_DEVICE)
+            if p.get("shard_ptrs") is not None:
+                arr = (ctypes.c_void_p * p["n_shards"])(*[x or None for x in p["shard_ptrs"]])
+                self._keep.append(arr)
+                pa[i].shard_ptrs = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        da = (wt_dst_meta * max(1, len(dsts)))()
+        for i, d in enumerate(dsts):
+            nm = d["name"].encode()
+            comps = (ctypes.c_char_p * len(d["components"]))(*[c.encode() for c in d["components"]])
+            self._keep += [nm, comps]
+            da[i].name = nm
+            da[i].components = ctypes.cast(comps, ctypes.POINTER(ctypes.c_char_p))
+            da[i].n_components = len(d["components"])
+            da[i].dtype = d["dtype"]
+        o = wt_schedule_options()
+        o.align, o.n_sources = align, n_sources
+        h = ctypes.c_void_p(0)
+        _check(lib.wt_schedule_build(pa, len(params), da, len(dsts), ctypes.byref(o), ctypes.byref(h)))
+        self.handle = h.value
+        self.n_dsts = len(dsts)
+
+    def info(self) -> dict:
+        nt, ns, nu = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        db = ctypes.c_uint64()
+        _check(lib.wt_schedule_info(self.handle, ctypes.byref(nt), ctypes.byref(ns), ctypes.byref(db), ctypes.byref(nu)))
+        return {"n_tasks": nt.value, "n_shards": ns.value, "dst_bytes": db.value, "n_unused_params": nu.value}
+
+    def output(self, i: int) -> dict:
+        do, so, ib = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+        src = ctypes.c_int32()
+        _check(lib.wt_schedule_output(self.handle, i, ctypes.byref(do), ctypes.byref(so), ctypes.byref(src),
+                                      ctypes.byref(ib)))
+        return {"dst_offset": do.value, "scale_offset": so.value, "source": src.value, "input_bytes": ib.value}
+
+    def tasks(self, source: int = -1) -> TaskTable:
+        nt, ns = ctypes.c_size_t(), ctypes.c_size_t()
+        st = lib.wt_schedule_tasks(self.handle, source, None, 0, None, 0, ctypes.byref(nt), ctypes.byref(ns))
+        if st not in (WT_OK, WT_E_RANGE):
+            _check(st)
+        tab = TaskTable([])
+        tab.arr = (wt_task * max(1, nt.value))()
+        sh = (wt_shard * max(1, ns.value))()
+        _check(lib.wt_schedule_tasks(self.handle, source, tab.arr, nt.value, sh, ns.value, ctypes.byref(nt),
+                                     ctypes.byref(ns)))
+        tab.n = nt.value
+        tab._shards = [sh]
+        return tab
+
+    def close(self) -> None:
+        if getattr(self, "handle", 0):
+            lib.wt_schedule_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ------------------------------------------------------------- workload glue

@@ -213,6 +213,76 @@ wt_status wt_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, int32_t 
  * (wrapping modulo 2^32), for i < count. out is a device pointer. */
 wt_status wt_cast_f32_range(uint32_t first, uint64_t count, uint8_t *out, void *stream);
 
+/* ---- Static schedule builder (host only) ----
+ * The controller's computation ("Weight transfer for RL post-training in
+ * under 2 seconds", section "High-level workflow": collect parameter
+ * metadata from training and inference, compute a static transfer schedule
+ * that says which training GPU sends which parameter where and in what
+ * order; section "Static schedule": computed once, replayed every step).
+ * Input: the training side's parameters (unique names, full shapes, FSDP
+ * dim-0 shard count and, optionally, shard addresses) and the inference
+ * side's tensors (names, the training parameters fused into each, in fusion
+ * order, and the output dtype). Output: destination offsets packed in the
+ * order of the inference tensors (data, then the FP8 scale grid, each
+ * aligned), the source GPU of every output (longest-processing-time-first
+ * over BF16 input bytes; ties to the lower index), and the task table that
+ * wt_plan_create takes, for all sources or one. Shards are the torch.chunk
+ * split of the rows: ceil(rows / n) rows each, trailing shards smaller or
+ * empty. */
+
+typedef struct wt_param_meta {
+  const char *name;              /* unique, NUL-terminated */
+  int64_t rows, cols;            /* full shape; a 1-D tensor of n elements is rows = n, cols = 1 */
+  int32_t n_shards;              /* FSDP dim-0 shards, >= 1 */
+  int32_t shard_mem;             /* WT_MEM_DEVICE or WT_MEM_PINNED_HOST */
+  const void *const *shard_ptrs; /* n_shards addresses, or NULL (tasks then carry NULL shard pointers) */
+} wt_param_meta;
+
+typedef struct wt_dst_meta {
+  const char *name;              /* inference-side tensor name */
+  const char *const *components; /* training parameter names, in fusion (dim-0 concatenation) order */
+  int32_t n_components;          /* >= 1; all components must have the same cols */
+  int32_t dtype;                 /* WT_FP8_E4M3FN_B128 or WT_BF16_COPY */
+} wt_dst_meta;
+
+typedef struct wt_schedule_options {
+  uint64_t align;    /* destination offset alignment, a power of two >= 16; 0 = 256 */
+  int32_t n_sources; /* source GPUs to balance outputs over; 0 = 1 */
+  int32_t reserved[5];
+} wt_schedule_options;
+
+typedef struct wt_schedule wt_schedule;
+
+/* Matches names, validates (unknown or duplicate names, cols that differ
+ * inside a fusion group, rows < 1: WT_E_INVAL), packs offsets and assigns
+ * sources. The inputs are copied. On failure *out is NULL and
+ * wt_plan_last_error(NULL) says why. */
+wt_status wt_schedule_build(const wt_param_meta *params, size_t n_params, const wt_dst_meta *dsts, size_t n_dsts,
+                            const wt_schedule_options *opts, wt_schedule **out);
+
+/* Totals: tasks (one per fusion component) and shard records over all
+ * sources, the destination region size, and how many training parameters no
+ * inference tensor uses. Any pointer may be NULL. */
+wt_status wt_schedule_info(const wt_schedule *sch, size_t *n_tasks, size_t *n_shards, uint64_t *dst_bytes,
+                           size_t *n_unused_params);
+
+/* Placement of inference tensor i: data and scale offsets (scale_offset is
+ * 0 for BF16 copies), its source GPU and its BF16 input bytes. */
+wt_status wt_schedule_output(const wt_schedule *sch, size_t i, uint64_t *dst_offset, uint64_t *scale_offset,
+                             int32_t *source, uint64_t *input_bytes);
+
+/* Writes the task table of one source (source = -1: every source) in
+ * inference-tensor order: tasks[0 .. *n_tasks) with their shard records in
+ * shards[]; task.shards points into the caller's shards array. Fusion
+ * groups are numbered by inference-tensor index. WT_E_RANGE if max_tasks or
+ * max_shards is too small (*n_tasks and *n_shards_out then give the sizes
+ * needed). */
+wt_status wt_schedule_tasks(const wt_schedule *sch, int32_t source, wt_task *tasks, size_t max_tasks,
+                            wt_shard *shards, size_t max_shards, size_t *n_tasks, size_t *n_shards_out);
+
+/* Frees the schedule. NULL is ignored. */
+void wt_schedule_destroy(wt_schedule *sch);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,3 +43,31 @@ def f32_to_bf16_bits_exact(x):
     u = np.asarray(x, dtype=np.float32).view(np.uint32)
     assert np.all((u & 0xFFFF) == 0), "value not exactly representable in BF16"
     return (u >> 16).astype(np.uint16)
+
+
+def schedule_example():
+    """tests/golden/schedule_example.txt as (params, dsts, expect, region, shards, unused);
+    expect maps a tensor to (dst_offset, scale_offset, source, input_bytes)."""
+    params, dsts, expect, shards = [], [], {}, {}
+    region = unused = None
+    with open(os.path.join(GOLDEN, "schedule_example.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0] == "param":
+                params.append({"name": tok[1], "rows": int(tok[2]), "cols": int(tok[3]), "n_shards": int(tok[4])})
+            elif tok[0] == "dst":
+                dsts.append({"name": tok[1], "dtype": 0 if tok[2] == "fp8" else 1, "components": tok[3:]})
+            elif tok[0] == "expect":
+                expect[tok[1]] = tuple(int(t) for t in tok[2:5])
+            elif tok[0] == "inbytes":
+                expect[tok[1]] = expect[tok[1]] + (int(tok[2]),)
+            elif tok[0] == "region":
+                region = int(tok[1])
+            elif tok[0] == "shards":
+                shards[tok[1]] = [int(t) for t in tok[2:]]
+            elif tok[0] == "unused":
+                unused = int(tok[1])
+    return params, dsts, expect, region, shards, unused
