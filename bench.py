@@ -116,6 +116,9 @@ def main() -> int:
     pipeline = None
     if wl.shard_mem == "host":
         pipeline = _h2d_ceiling(wl, ms_per_step, args.steps)
+    if info["n_units"] > 1:
+        pipeline = pipeline or {}
+        pipeline["progress"] = _progress_timeline(plan, info["n_units"], sp)
 
     traffic = None
     try:
@@ -198,6 +201,34 @@ def _h2d_ceiling(wl, ms_per_step: float, steps: int) -> dict:
            "arena_bytes": int(arena.numel())}
     log(f"pipeline: bare H2D of the {arena.numel() / 1e9:.3f} GB arena {t_h2d:.3f} ms "
         f"({out['h2d_GBps']} GB/s); pipeline {ms_per_step:.3f} ms; overlap efficiency {out['overlap_eff']}")
+    return out
+
+
+def _progress_timeline(plan, n_units: int, stream: int) -> dict:
+    """One more replay with completion counters attached: the host polls each
+    unit's word in order and records when it saw it, i.e. when that part of
+    the destination region could start its transfer."""
+    import torch
+    from bf16_fp8_weight_amd import wt
+
+    words = torch.zeros(n_units, dtype=torch.int64).pin_memory()
+    wt.wt_plan_set_progress(plan.handle, words.data_ptr(), n_units)
+    torch.cuda.synchronize()
+    seen = []
+    t0 = time.perf_counter()
+    plan.prepare(stream)
+    for u in range(n_units):
+        if not wt.wt_progress_wait(words.data_ptr() + 8 * u, 1, 60 * 10**9):
+            raise RuntimeError(f"completion unit {u} not reached within 60 s")
+        seen.append((time.perf_counter() - t0) * 1e3)
+    torch.cuda.synchronize()
+    t_sync = (time.perf_counter() - t0) * 1e3
+    wt.wt_plan_set_progress(plan.handle, 0, 0)
+    gaps = sorted(b - a for a, b in zip(seen, seen[1:])) or [0.0]
+    out = {"units": n_units, "first_unit_ms": round(seen[0], 3), "last_unit_ms": round(seen[-1], 3),
+           "median_gap_ms": round(gaps[len(gaps) // 2], 3), "replay_sync_ms": round(t_sync, 3)}
+    log(f"progress: {n_units} units; first seen by the host at {seen[0]:.3f} ms, last at {seen[-1]:.3f} ms, "
+        f"replay synchronized at {t_sync:.3f} ms")
     return out
 
 

@@ -297,6 +297,18 @@ wt_status build_layout(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, i
   }
   I.staging_bytes = L->staging_bytes;
 
+  // completion units: the direct launch first (when present), then each chunk
+  {
+    const int32_t base = L->direct.empty() ? 0 : 1;
+    std::vector<int32_t> out_unit(L->outs.size(), 0);
+    for (size_t c = 0; c < L->chunks.size(); ++c)
+      for (int32_t o : L->chunks[c].outputs) out_unit[o] = base + (int32_t)c;
+    L->task_unit.assign(n_tasks, 0);
+    for (size_t o = 0; o < out_tasks.size(); ++o)
+      for (int32_t t : out_tasks[o]) L->task_unit[t] = out_unit[o];
+    I.n_units = base + (int64_t)L->chunks.size();
+  }
+
   // Launch count: resolve addresses against aligned virtual bases (the
   // destination and staging bases are 256-byte aligned in a real plan).
   struct VirtAddr : BatchAddr {

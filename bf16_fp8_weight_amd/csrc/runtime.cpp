@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -29,6 +30,8 @@ hipError_t launch_batch(const LaunchTables &T, hipStream_t stream);
 hipError_t launch_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, uint8_t *out, int variant,
                                   hipStream_t stream);
 hipError_t launch_cast_range(uint32_t first, uint64_t count, uint8_t *out, hipStream_t stream);
+hipError_t launch_progress_begin(uint64_t *epoch, hipStream_t stream);
+hipError_t launch_progress_mark(const uint64_t *epoch, uint64_t *word, hipStream_t stream);
 }  // namespace wt
 
 using namespace wt;
@@ -42,6 +45,8 @@ struct wt_plan {
   bool pipeline = false;
 
   uint8_t *tables = nullptr;  // every batch's device tables, one allocation
+  uint64_t *epoch = nullptr;  // replay counter (device, inside the tables allocation)
+  uint64_t *progress = nullptr;  // caller's completion words (pinned host), or null
   uint8_t *staging = nullptr;
   std::vector<LaunchTables> batches;  // [0] = direct batch when present, then one per chunk
   int direct_batch = -1;
@@ -245,7 +250,8 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
   for (const HostTables &t : hts)
     total += blob_bytes(t.outs) + blob_bytes(t.segs) + blob_bytes(t.fast) + blob_bytes(t.edge) +
              blob_bytes(t.general) + blob_bytes(t.copies);
-  total = std::max<size_t>(total, 256);
+  const size_t epoch_off = total;
+  total += 256;
   std::vector<uint8_t> blob(total, 0);
   HIP_OR(p, hipMalloc((void **)&p->tables, total));
   size_t off = 0;
@@ -275,6 +281,7 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
     T.n_copies = (uint32_t)t.copies.size();
     p->batches.push_back(T);
   }
+  p->epoch = (uint64_t *)(p->tables + epoch_off);
   HIP_OR(p, hipMemcpy(p->tables, blob.data(), total, hipMemcpyHostToDevice));
 
   if (p->pipeline) {
@@ -299,10 +306,14 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
 
 wt_status prepare_impl(wt_plan *p, hipStream_t user) {
   const Layout &L = p->L;
+  const bool progress = p->progress != nullptr;
+  if (progress) HIP_OR(p, launch_progress_begin(p->epoch, user));
   if (!p->pipeline) {
     HIP_OR(p, launch_batch(p->batches[p->direct_batch], user));
+    if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress, user));
     return WT_OK;
   }
+  const int unit_base = p->direct_batch >= 0 ? 1 : 0;
   const bool staged = L.dst_mode == WT_DST_STAGED;
   const hipMemcpyKind out_kind = p->dst_kind == WT_MEM_DEVICE ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
 
@@ -312,7 +323,10 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
     HIP_OR(p, hipStreamWaitEvent(s, p->ev_start, 0));
     if (p->has_prev) HIP_OR(p, hipStreamWaitEvent(s, p->ev_done, 0));
   }
-  if (p->direct_batch >= 0) HIP_OR(p, launch_batch(p->batches[p->direct_batch], p->s_prep));
+  if (p->direct_batch >= 0) {
+    HIP_OR(p, launch_batch(p->batches[p->direct_batch], p->s_prep));
+    if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress, p->s_prep));
+  }
 
   for (size_t c = 0; c < L.chunks.size(); ++c) {
     const Chunk &C = L.chunks[c];
@@ -336,8 +350,10 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
       for (const DstCopy &d : C.dst_copies)
         HIP_OR(p, hipMemcpyAsync(p->dst + d.dst_off, p->staging + C.slot_off + d.stage_off, (size_t)d.bytes,
                                  out_kind, p->s_out));
+      if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress + unit_base + c, p->s_out));
       HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_out));
     } else {
+      if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress + unit_base + c, p->s_prep));
       HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_prep));
     }
   }
@@ -496,6 +512,71 @@ wt_status wt_plan_get_info(const wt_plan *plan, wt_plan_info *info) {
   return WT_OK;
 }
 
+wt_status wt_plan_set_progress(wt_plan *plan, uint64_t *words, size_t n_words) {
+  if (!plan) return WT_E_INVAL;
+  bool expected = false;
+  if (!plan->busy.compare_exchange_strong(expected, true)) {
+    set_err(plan, "wt_prepare running on this plan");
+    return WT_E_STATE;
+  }
+  wt_status st = WT_OK;
+  try {
+    DeviceGuard guard(plan->device);
+    const size_t need = (size_t)plan->L.info.n_units;
+    std::string err;
+    if (!words) {
+      plan->progress = nullptr;
+    } else if ((uintptr_t)words % 8) {
+      set_err(plan, "progress words not 8-byte aligned");
+      st = WT_E_INVAL;
+    } else if (n_words < need) {
+      set_err(plan, "progress words: " + std::to_string(n_words) + " given, " + std::to_string(need) + " units");
+      st = WT_E_INVAL;
+    } else if ((st = check_memory(words, 8 * need, WT_MEM_PINNED_HOST, plan->device, "progress words", &err)) !=
+               WT_OK) {
+      set_err(plan, err);
+    } else {
+      // reset the replay counter; no replay of this plan is in flight
+      const uint64_t zero = 0;
+      hipError_t e = hipMemcpy(plan->epoch, &zero, sizeof zero, hipMemcpyHostToDevice);
+      if (e != hipSuccess) {
+        set_err(plan, hip_msg("hipMemcpy(epoch)", e));
+        st = WT_E_HIP;
+      } else {
+        plan->progress = words;
+      }
+    }
+  } catch (...) {
+    set_err(plan, "internal error");
+    st = WT_E_INVAL;
+  }
+  plan->busy.store(false);
+  return st;
+}
+
+wt_status wt_plan_task_unit(const wt_plan *plan, size_t task, int32_t *unit) {
+  if (!plan || !unit || task >= plan->L.task_unit.size()) return WT_E_INVAL;
+  *unit = plan->L.task_unit[task];
+  return WT_OK;
+}
+
+wt_status wt_progress_wait(const uint64_t *word, uint64_t target, uint64_t timeout_ns) {
+  if (!word) return WT_E_INVAL;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (uint32_t spin = 0;; ++spin) {
+    if (__atomic_load_n(word, __ATOMIC_ACQUIRE) >= target) return WT_OK;
+    if ((spin & 255u) == 0) {
+      const auto dt = std::chrono::steady_clock::now() - t0;
+      if ((uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(dt).count() >= timeout_ns) {
+        return __atomic_load_n(word, __ATOMIC_ACQUIRE) >= target ? WT_OK : WT_E_TIMEOUT;
+      }
+    }
+#if defined(__x86_64__)
+    __builtin_ia32_pause();
+#endif
+  }
+}
+
 void wt_plan_destroy(wt_plan *plan) {
   if (!plan) return;
   {
@@ -516,6 +597,7 @@ const char *wt_status_str(int status) {
     case WT_E_HIP: return "WT_E_HIP: HIP runtime error";
     case WT_E_WATERMARK: return "WT_E_WATERMARK: watermark below one output's staging need";
     case WT_E_STATE: return "WT_E_STATE: plan busy";
+    case WT_E_TIMEOUT: return "WT_E_TIMEOUT: progress word did not reach its target in time";
     default: return "unknown status";
   }
 }

@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("WT_LIB") or os.path.join(PKG, "libwt.so")
 
 WT_OK = 0
-WT_E_INVAL, WT_E_RANGE, WT_E_OVERLAP, WT_E_ALIGN, WT_E_NOMEM, WT_E_HIP, WT_E_WATERMARK, WT_E_STATE = range(1, 9)
+(WT_E_INVAL, WT_E_RANGE, WT_E_OVERLAP, WT_E_ALIGN, WT_E_NOMEM, WT_E_HIP, WT_E_WATERMARK, WT_E_STATE,
+ WT_E_TIMEOUT) = range(1, 10)
 WT_FP8_E4M3FN_B128 = 0
 WT_BF16_COPY = 1
 WT_MEM_DEVICE = 0
@@ -29,6 +30,7 @@ EXPORTS = [
     "wt_plan_get_info", "wt_plan_destroy", "wt_status_str", "wt_plan_last_error",
     "wt_quantize_domain", "wt_cast_f32_range",
     "wt_schedule_build", "wt_schedule_info", "wt_schedule_output", "wt_schedule_tasks", "wt_schedule_destroy",
+    "wt_plan_set_progress", "wt_plan_task_unit", "wt_progress_wait",
 ]
 
 
@@ -62,7 +64,8 @@ class wt_plan_options(ctypes.Structure):
 class wt_plan_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "n_tasks", "n_outputs", "n_fp8_outputs", "n_copy_outputs", "n_tiles", "input_bytes", "output_bytes",
-        "n_launches", "n_chunks", "n_h2d_copies", "n_dst_copies", "staging_bytes")] + [("reserved", ctypes.c_int64 * 4)]
+        "n_launches", "n_chunks", "n_h2d_copies", "n_dst_copies", "staging_bytes", "n_units")] + [
+        ("reserved", ctypes.c_int64 * 3)]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_ if n != "reserved"}
@@ -144,6 +147,12 @@ def _load() -> ctypes.CDLL:
     L.wt_schedule_tasks.argtypes = [vp, i32, P(wt_task), sz, P(wt_shard), sz, P(sz), P(sz)]
     L.wt_schedule_destroy.restype = None
     L.wt_schedule_destroy.argtypes = [vp]
+    L.wt_plan_set_progress.restype = ctypes.c_int
+    L.wt_plan_set_progress.argtypes = [vp, vp, sz]
+    L.wt_plan_task_unit.restype = ctypes.c_int
+    L.wt_plan_task_unit.argtypes = [vp, sz, P(i32)]
+    L.wt_progress_wait.restype = ctypes.c_int
+    L.wt_progress_wait.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint64]
     return L
 
 
@@ -240,6 +249,26 @@ def wt_plan_get_info(plan: int) -> dict:
     info = wt_plan_info()
     _check(lib.wt_plan_get_info(plan, ctypes.byref(info)), plan)
     return info.as_dict()
+
+
+def wt_plan_set_progress(plan: int, words: int, n_words: int) -> None:
+    """words: address of n_words uint64 in pinned host memory (0 detaches)."""
+    _check(lib.wt_plan_set_progress(plan, words or None, n_words), plan)
+
+
+def wt_plan_task_unit(plan: int, task: int) -> int:
+    u = ctypes.c_int32()
+    _check(lib.wt_plan_task_unit(plan, task, ctypes.byref(u)), plan)
+    return u.value
+
+
+def wt_progress_wait(word: int, target: int, timeout_ns: int) -> bool:
+    """True once *word >= target, False on timeout."""
+    st = lib.wt_progress_wait(word or None, target, timeout_ns)
+    if st == WT_E_TIMEOUT:
+        return False
+    _check(st)
+    return True
 
 
 def wt_plan_destroy(plan: int) -> None:

@@ -48,7 +48,8 @@ typedef enum wt_status {
   WT_E_NOMEM = 5,     /* host or device allocation failed */
   WT_E_HIP = 6,       /* HIP runtime error; text from wt_plan_last_error() */
   WT_E_WATERMARK = 7, /* watermark below the staging need of one output */
-  WT_E_STATE = 8      /* wt_prepare already running on this plan */
+  WT_E_STATE = 8,     /* wt_prepare already running on this plan */
+  WT_E_TIMEOUT = 9    /* wt_progress_wait: the word did not reach its target in time */
 } wt_status;
 
 /* Output data type of a task (and of its fusion group). */
@@ -126,7 +127,8 @@ typedef struct wt_plan_info {
   int64_t n_h2d_copies;       /* host-to-device copies per wt_prepare */
   int64_t n_dst_copies;       /* staging-to-destination copies per wt_prepare */
   int64_t staging_bytes;      /* device staging allocated (<= watermark) */
-  int64_t reserved[4];
+  int64_t n_units;            /* completion units: the device-resident launch (if any), then each chunk */
+  int64_t reserved[3];
 } wt_plan_info;
 
 /* One operation of the replayed schedule, as listed by wt_plan_schedule. */
@@ -282,6 +284,40 @@ wt_status wt_schedule_tasks(const wt_schedule *sch, int32_t source, wt_task *tas
 
 /* Frees the schedule. NULL is ignored. */
 void wt_schedule_destroy(wt_schedule *sch);
+
+/* ---- Completion counters ----
+ * Host-visible words that the GPU writes as parts of a replay finish, so a
+ * host thread can start moving a part of the destination region (the one-sided
+ * write to the inference side) as soon as it is final instead of waiting for
+ * the whole replay ("RDMA point-to-point communication for LLM systems",
+ * GPU-progress notification through memory words that kernels update and the
+ * CPU polls; receiver-side counters per index). A replay finishes in units: the
+ * launch over device-resident outputs (unit 0 when the plan has one), then
+ * each pipeline chunk in order; wt_plan_info.n_units counts them and
+ * wt_plan_task_unit maps a task to its unit. */
+
+/* Attaches `words` (n_words >= n_units 8-byte words in pinned host memory,
+ * 8-byte aligned; owned by the caller, who must keep it alive while the plan
+ * replays) to the plan and resets the plan's replay counter. From then on the
+ * r-th wt_prepare (r = 1, 2, ...) stores r into words[u] once every byte of
+ * unit u is in the destination region: after the unit's prepare launch
+ * (zero-copy) or after its destination copies (WT_DST_STAGED). The stores are
+ * made by a one-thread kernel on the stream that ran the unit, with release
+ * ordering at system scope, behind the unit's work. Passing words == NULL
+ * detaches. Call only while no replay of this plan is in flight. The words are
+ * never cleared by the library. WT_E_INVAL for a short, misaligned or
+ * non-pinned array. */
+wt_status wt_plan_set_progress(wt_plan *plan, uint64_t *words, size_t n_words);
+
+/* *unit = the completion unit that covers task `task` (index into the table
+ * given to wt_plan_create). WT_E_INVAL if task is out of range. */
+wt_status wt_plan_task_unit(const wt_plan *plan, size_t task, int32_t *unit);
+
+/* Host-side wait: polls *word (acquire loads) until it is >= target or
+ * timeout_ns elapses. WT_OK when reached (the unit's bytes are then visible to
+ * the host), WT_E_TIMEOUT otherwise, WT_E_INVAL for a NULL word. Makes no HIP
+ * call. */
+wt_status wt_progress_wait(const uint64_t *word, uint64_t target, uint64_t timeout_ns);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_exports_match_header(wt):
 
 def test_status_strings(wt):
     assert wt.wt_status_str(0) == "WT_OK"
-    for s in range(1, 9):
+    for s in range(1, 10):
         assert wt.wt_status_str(s).startswith("WT_E_")
 
 
@@ -180,3 +180,45 @@ def test_gapped_host_shards_copy_per_run(wt):
     tab = fake_table(wt, wl, gap=512, host=True)
     info = wt.wt_plan_check(tab, wl.dst_bytes, opts=o)
     assert info["n_h2d_copies"] == 8  # no merging across gaps
+
+
+def test_completion_units(wt):
+    # device-resident zero-copy: the one launch is the one unit
+    wl = W.dense_layer_h1024(materialize=False)
+    assert wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)["n_units"] == 1
+    # pinned-host shards: one unit per chunk
+    wl = W.mla_many_small(materialize=False, layers=1, n_small=300, host=True)
+    o = wt.wt_plan_options_init()
+    o.chunk_bytes = 8 << 20
+    i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes, wt.WT_MEM_PINNED_HOST, o)
+    assert i["n_units"] == i["n_chunks"] > 1
+    # mixed: device-resident outputs launch first as unit 0, then the chunks
+    wl = W.mla_many_small(materialize=False, layers=1, n_small=300, host=True)
+    tab = fake_table(wt, wl).as_dicts()
+    for t in tab[:3]:
+        t["shard_mem"] = wt.WT_MEM_DEVICE
+    i = wt.wt_plan_check(wt.TaskTable(tab), wl.dst_bytes, wt.WT_MEM_PINNED_HOST, o)
+    assert i["n_units"] == i["n_chunks"] + 1
+
+
+def test_progress_wait_on_the_host(wt):
+    import ctypes
+    import threading
+    import time
+
+    w = (ctypes.c_uint64 * 2)(7, 0)
+    a = ctypes.addressof(w)
+    assert wt.wt_progress_wait(a, 7, 0) and wt.wt_progress_wait(a, 3, 10)
+    t0 = time.perf_counter()
+    assert not wt.wt_progress_wait(a, 8, 20 * 10**6)
+    assert 0.015 < time.perf_counter() - t0 < 5
+    with pytest.raises(wt.WtError):
+        wt.wt_progress_wait(0, 1, 10)
+
+    def later():
+        time.sleep(0.05)
+        w[1] = 1
+    th = threading.Thread(target=later)
+    th.start()
+    assert wt.wt_progress_wait(a + 8, 1, 10 * 10**9)
+    th.join()
