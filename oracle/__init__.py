@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_cast_f32_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.oracle_quantize_elements.restype = None
         L.oracle_quantize_elements.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p]
+        L.oracle_quantize_act_b128.restype = ctypes.c_int
+        L.oracle_quantize_act_b128.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.c_void_p, ctypes.c_int64]
         _lib = L
     return _lib
 
@@ -192,3 +196,36 @@ def prepare(outputs: Sequence[Output], dst_bytes: int, dst: np.ndarray | None = 
     if rc != 0:
         raise ValueError("oracle_prepare failed with code %d" % rc)
     return dst
+
+
+def quantize_act(x: np.ndarray, cols: int | None = None, index=None, n_out: int | None = None,
+                 q: np.ndarray | None = None, scales: np.ndarray | None = None):
+    """oracle_quantize_act_b128 on a host array.
+
+    x: uint16 BF16 bits [n_rows, x_stride]; cols (default x_stride) columns
+    used. index: int32 output-row -> input-row map, or None. q: uint8
+    [n_out, q_stride] and scales: uint8 [n_out, s_stride] (pre-filled for
+    canary checks) or None for zero-filled [n_out, cols] and
+    [n_out, 4 ceil(cols / 128)]. Returns (q, scales as float32 view when
+    s_stride is 4 ceil(cols / 128), else the raw bytes).
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    assert x.ndim == 2
+    n_rows, x_stride = x.shape
+    cols = x_stride if cols is None else cols
+    idx = None if index is None else np.ascontiguousarray(index, dtype=np.int32)
+    n_out = (n_rows if idx is None else idx.size) if n_out is None else n_out
+    nb = -(-cols // 128)
+    if q is None:
+        q = np.zeros((n_out, cols), dtype=np.uint8)
+    if scales is None:
+        scales = np.zeros((n_out, 4 * nb), dtype=np.uint8)
+    assert q.dtype == np.uint8 and q.flags.c_contiguous and q.shape[0] == n_out
+    assert scales.dtype == np.uint8 and scales.flags.c_contiguous and scales.shape[0] == n_out
+    rc = lib().oracle_quantize_act_b128(_ptr(x) if x.size else None, n_rows, cols, x_stride,
+                                        _ptr(idx) if idx is not None else None, n_out,
+                                        _ptr(q), q.shape[1], _ptr(scales), scales.shape[1])
+    if rc != 0:
+        raise ValueError("oracle_quantize_act_b128 failed with code %d" % rc)
+    sv = scales.view(np.float32) if scales.shape[1] == 4 * nb else scales
+    return q, sv

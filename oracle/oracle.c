@@ -237,3 +237,29 @@ void oracle_cast_f32_array(const float *in, int64_t n, uint8_t *out) {
 void oracle_quantize_elements(const uint16_t *x_bits, int64_t n, float s, uint8_t *out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_quantize_element(x_bits[i], s);
 }
+
+int oracle_quantize_act_b128(const uint16_t *x, int64_t n_rows, int64_t cols, int64_t x_stride,
+                             const int32_t *index, int64_t n_out, uint8_t *q, int64_t q_stride,
+                             uint8_t *scales, int64_t s_stride) {
+  if (n_rows < 0 || cols < 1 || n_out < 0 || x_stride < cols || q_stride < cols) return ORACLE_E_ARG;
+  const int64_t nb = (cols + 127) / 128;
+  if (s_stride < 4 * nb) return ORACLE_E_ARG;
+  if (n_out > 0 && (!q || !scales || (n_rows > 0 && !x))) return ORACLE_E_ARG;
+  for (int64_t i = 0; i < n_out; ++i) {
+    const int64_t src = index ? (int64_t)index[i] : i;
+    if (src < 0 || src >= n_rows) continue;
+    const uint16_t *xr = x + src * x_stride;
+    for (int64_t b = 0; b < nb; ++b) {
+      const int64_t c0 = 128 * b, c1 = (c0 + 128 < cols) ? c0 + 128 : cols;
+      float amax = 0.0f;
+      for (int64_t c = c0; c < c1; ++c) {
+        const float a = fabsf(oracle_bf16_to_f32(xr[c]));
+        if (a > amax) amax = a;
+      }
+      const float s = oracle_tile_scale(amax);
+      for (int64_t c = c0; c < c1; ++c) q[i * q_stride + c] = oracle_quantize_element(xr[c], s);
+      memcpy(scales + i * s_stride + 4 * b, &s, sizeof s);
+    }
+  }
+  return ORACLE_OK;
+}

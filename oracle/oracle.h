@@ -107,6 +107,21 @@ void oracle_cast_f32_array(const float *in, int64_t n, uint8_t *out);
 /* out[i] = oracle_quantize_element(x_bits[i], s). */
 void oracle_quantize_elements(const uint16_t *x_bits, int64_t n, float s, uint8_t *out);
 
+/* Block-scaled FP8 quantization of token activations ("Enabling
+ * trillion-parameter models on AWS EFA", dispatch/combine evaluation: hidden
+ * size 7168, FP8 dispatch with block scales). Readings: a block is 1 x 128
+ * (one token, 128 consecutive channels; the last block of a row holds the
+ * remaining cols % 128 channels), with the weight tiles' scale and element
+ * arithmetic. Output row i quantizes input row index[i] (row i when index is
+ * NULL); an output row whose index lies outside [0, n_rows) is left
+ * untouched. x: n_rows rows of x_stride BF16 elements (the first cols used).
+ * q: n_out rows of q_stride bytes, the row's cols FP8 bytes first. scales:
+ * n_out rows of s_stride bytes, the row's ceil(cols / 128) fp32 scales first.
+ * Bytes past cols (q) and past the scales (scales) are left untouched. */
+int oracle_quantize_act_b128(const uint16_t *x, int64_t n_rows, int64_t cols, int64_t x_stride,
+                             const int32_t *index, int64_t n_out, uint8_t *q, int64_t q_stride,
+                             uint8_t *scales, int64_t s_stride);
+
 #ifdef __cplusplus
 }
 #endif

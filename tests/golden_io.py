@@ -71,3 +71,28 @@ def schedule_example():
             elif tok[0] == "unused":
                 unused = int(tok[1])
     return params, dsts, expect, region, shards, unused
+
+
+def act_blocks():
+    """tests/golden/act_blocks.txt as a list of dicts {name, cols, x, bytes, scale_bits}."""
+    rows, cur = [], None
+    with open(os.path.join(GOLDEN, "act_blocks.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            if tok[0] == "row":
+                cur = {"name": tok[1], "cols": int(tok[2])}
+                rows.append(cur)
+            elif tok[0] == "x":
+                x = np.zeros(cur["cols"], dtype=np.uint16)
+                for t in tok[1:]:
+                    c, v = t.split(":")
+                    x[int(c)] = int(v, 16)
+                cur["x"] = x
+            elif tok[0] == "bytes":
+                cur["bytes"] = {int(c): int(v, 16) for c, v in (t.split(":") for t in tok[1:])}
+            elif tok[0] == "scale_bits":
+                cur["scale_bits"] = [int(t, 16) for t in tok[1:]]
+    return rows

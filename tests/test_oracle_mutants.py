@@ -43,9 +43,19 @@ MUTANTS = [
     ("components_overwrite", "fused_row += Rc;", "fused_row += 0;"),
     ("tile_rows_127", "const int64_t r0 = 128 * I, r1 = (128 * I + 128 < R) ? 128 * I + 128 : R;",
      "const int64_t r0 = 128 * I, r1 = (128 * I + 127 < R) ? 128 * I + 127 : R;"),
+    # block-scaled activations
+    ("act_block_127", "const int64_t c0 = 128 * b, c1 = (c0 + 128 < cols) ? c0 + 128 : cols;",
+     "const int64_t c0 = 128 * b, c1 = (c0 + 127 < cols) ? c0 + 127 : cols;"),
+    ("act_index_ignored", "const int64_t src = index ? (int64_t)index[i] : i;", "const int64_t src = i < n_rows ? i : 0;"),
+    ("act_scales_packed", "memcpy(scales + i * s_stride + 4 * b, &s, sizeof s);",
+     "memcpy(scales + i * 4 * nb + 4 * b, &s, sizeof s);"),
+    ("act_amax_signed", "const float a = fabsf(oracle_bf16_to_f32(xr[c]));", "const float a = oracle_bf16_to_f32(xr[c]);"),
+    ("act_q_dense_rows", "q[i * q_stride + c] = oracle_quantize_element(xr[c], s);",
+     "q[i * cols + c] = oracle_quantize_element(xr[c], s);"),
 ]
 
-PIN_FILES = ["tests/test_oracle_cast.py", "tests/test_oracle_quant.py", "tests/test_oracle_prepare.py"]
+PIN_FILES = ["tests/test_oracle_cast.py", "tests/test_oracle_quant.py", "tests/test_oracle_prepare.py",
+             "tests/test_oracle_act.py"]
 
 
 def _run_mutant(name, old, new, tmp):
