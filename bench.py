@@ -36,7 +36,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="kimi_k2_moe",
                     choices=["kimi_k2_moe", "dense_7b", "dense_layer_h1024", "ragged_stress", "mla_many_small",
-                             "mla_many_small_device"])
+                             "mla_many_small_device", "act_dispatch_decode", "act_tokens_4096"])
     ap.add_argument("--dst-mode", default="zero-copy", choices=["zero-copy", "staged"],
                     help="how prepared bytes reach the destination region")
     ap.add_argument("--dst-kind", default="device", choices=["device", "pinned"],
@@ -62,6 +62,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         return _copy_calibration(args.calibrate_copy, args.steps, args.warmup)
+    if args.workload.startswith("act_"):
+        return _bench_act(args)
     t0 = time.time()
     if args.workload == "mla_many_small_device":
         wl = W.mla_many_small(device="cuda", host=False)
@@ -296,6 +298,105 @@ def _cpu_baseline(wl, dst, threads):
         "sample": f"the whole workload ({len(outs)} outputs, {wl.input_bytes} B BF16), one thread per output",
         "seconds": round(dt, 2),
     }, ok
+
+
+def _bench_act(args) -> int:
+    """Block-scaled FP8 quantization of token activations: one launch per
+    step, timed with HIP events on the launch stream around every launch."""
+    import numpy as np
+    import torch
+    from bf16_fp8_weight_amd import workloads as W
+    from bf16_fp8_weight_amd import wt
+
+    if args.workload == "act_dispatch_decode":
+        wl = W.act_dispatch(device="cuda")
+    else:
+        wl = W.act_tokens(device="cuda", tokens=4096)
+    H, n_out = wl.hidden, wl.n_out
+    if wl.interleaved:
+        buf = torch.full((n_out * wl.slot,), 0xA5, dtype=torch.uint8, device="cuda")
+        q_ptr, s_ptr = buf.data_ptr(), buf.data_ptr() + H
+    else:
+        qt = torch.full((n_out * H,), 0xA5, dtype=torch.uint8, device="cuda")
+        st = torch.full((n_out * 4 * wl.nb,), 0xA5, dtype=torch.uint8, device="cuda")
+        q_ptr, s_ptr = qt.data_ptr(), st.data_ptr()
+    idx_ptr = wl.index.data_ptr() if wl.index is not None else 0
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def launch():
+        wt.wt_quantize_act_b128(wl.x.data_ptr(), wl.tokens, H, H, idx_ptr, n_out, q_ptr, wl.q_stride, s_ptr,
+                                wl.s_stride, sp)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg_s = sum(launch_ms) / len(launch_ms) / 1e3
+    value = wl.input_bytes / avg_s / 1e9
+    achieved = wl.algorithmic_bytes / avg_s / 1e9
+    log(f"{wl.name}: {n_out} rows; launch avg {avg_s * 1e6:.2f} us (min {min(launch_ms) * 1e3:.2f}); "
+        f"wall {t_total / args.steps * 1e6:.2f} us/step; HBM {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.3f}")
+
+    cpu = None
+    verified = None
+    if not args.no_cpu_baseline:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import oracle
+
+        oracle.build(force=False)
+        x = wl.x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        idx = wl.index.cpu().numpy() if wl.index is not None else None
+        nb = wl.nb
+        wq = np.full((n_out, H), 0xA5, dtype=np.uint8)
+        ws = np.full((n_out, 4 * nb), 0xA5, dtype=np.uint8)
+        t1 = time.perf_counter()
+        oracle.quantize_act(x, cols=H, index=idx, n_out=n_out, q=wq, scales=ws)
+        dt = time.perf_counter() - t1
+        if wl.interleaved:
+            got = buf.cpu().numpy().reshape(n_out, wl.slot)
+            gq, gs = got[:, :H], got[:, H:H + 4 * nb]
+        else:
+            gq, gs = qt.cpu().numpy().reshape(n_out, H), st.cpu().numpy().reshape(n_out, 4 * nb)
+        verified = bool(np.array_equal(gq, wq) and np.array_equal(gs, ws))
+        cpu = {"value": round(wl.input_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole workload ({n_out} rows x {H}), one thread", "seconds": round(dt, 3)}
+        log(f"cpu baseline: oracle {dt:.3f}s; GPU output {'identical to' if verified else 'DIFFERS from'} the oracle")
+
+    line = {
+        "metric": "quantized BF16 activation GB/s (1x128 block-scaled FP8, gather into send slots) and % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(avg_s * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded Student-t(3) activations with 8 outlier channels x50",
+        "config": {"workload": wl.name, "tokens": wl.tokens, "hidden": H, "rows_out": n_out,
+                   "layout": "interleaved send slots" if wl.interleaved else "separate codes and scales"},
+        "pct_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": wl.algorithmic_bytes, "avg_launch_ms": round(avg_s * 1e3, 6),
+                     "launches_per_step": 1},
+        "cpu_baseline": cpu,
+        "verified_vs_oracle": verified,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if verified in (None, True) else 1
 
 
 if __name__ == "__main__":

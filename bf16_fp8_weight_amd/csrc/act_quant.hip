@@ -1,0 +1,101 @@
+// act_quant.hip -- block-scaled FP8 quantization of token activations
+// ("Enabling trillion-parameter models on AWS EFA", dispatch/combine
+// evaluation: hidden size 7168, FP8 dispatch with block scales). A block is
+// one token's 128 consecutive channels (the last block of a row may be
+// shorter); per block s = amax / 448 (1 for an all-zero block) and
+// q = cast(fl32(x / s)) with the same element arithmetic as the weight tiles.
+// Output row i quantizes input row index[i] (row i without an index), which
+// fuses the sender's shuffle of tokens into send-buffer slots with the
+// quantization; rows whose index is out of range are skipped.
+//
+// Mapping: one 16-lane DPP row per block, lane l owns channels
+// [128 b + 8 l, +8): one 16-byte load and one 8-byte store per lane, so a
+// wave reads four blocks (1 KB) and writes 512 bytes per instruction. The
+// block's amax is a butterfly max over the 16 lanes (quad_perm, row half
+// mirror, row mirror), which leaves it in every lane of the row.
+#include <hip/hip_runtime.h>
+
+#include "fp8_math.h"
+#include "wt_internal.h"
+
+namespace wt {
+namespace {
+
+constexpr int kActThreads = 256;
+constexpr int kActBlocksPerWG = kActThreads / 16;
+
+__device__ __forceinline__ uint32_t row16_max(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x0B1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x04E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));  // row_mirror
+  return m;
+}
+
+template <bool Recip>
+__device__ __forceinline__ uint2 quant8(const uint32_t w[4], const TileQ &t) {
+  return make_uint2(quant4<Recip>(w[0], w[1], t), quant4<Recip>(w[2], w[3], t));
+}
+
+// Fast: cols, x_stride, q_stride multiples of 8, x 16-byte and q 8-byte
+// aligned. General: any shape and alignment (2-byte loads, byte stores).
+template <bool Fast>
+__global__ void __launch_bounds__(kActThreads) act_quant_kernel(ActArgs a) {
+  const uint32_t gblk = blockIdx.x * (uint32_t)kActBlocksPerWG + (threadIdx.x >> 4);
+  const uint32_t l = threadIdx.x & 15;
+  bool valid = gblk < a.n_blocks;
+  uint32_t i = 0, b = 0;
+  int64_t src = -1;
+  if (valid) {
+    i = gblk / a.nb;
+    b = gblk - i * a.nb;
+    src = a.index ? (int64_t)ld_global<int32_t>(a.index + 4ull * i) : (int64_t)i;
+    valid = src >= 0 && src < a.n_rows;
+  }
+  const int64_t c = 128 * (int64_t)b + 8 * (int64_t)l;
+  const bool has = valid && c < a.cols;
+  const uint64_t xrow = a.x + 2ull * (uint64_t)src * (uint64_t)a.x_stride;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (Fast) {
+    if (has) {
+      const uint4 v = ld_global<uint4>(xrow + 2ull * (uint64_t)c);
+      w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
+    }
+  } else if (has) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (c + e < a.cols) w[e >> 1] |= (uint32_t)ld_global<uint16_t>(xrow + 2ull * (uint64_t)(c + e)) << (16 * (e & 1));
+  }
+  uint32_t m = pk_max_u16(pk_max_u16(abs2(w[0]), abs2(w[1])), pk_max_u16(abs2(w[2]), abs2(w[3])));
+  m = row16_max(max(m & 0xFFFFu, m >> 16));  // every lane of the row takes part
+  if (!has) return;
+  const TileQ t = block_quant(m);
+  const uint64_t qrow = a.q + (uint64_t)i * (uint64_t)a.q_stride;
+  if (Fast) {
+    const uint2 q = t.recip ? quant8<true>(w, t) : quant8<false>(w, t);
+    st_global<uint2>(qrow + (uint64_t)c, q);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (c + e < a.cols) {
+        const uint32_t xb = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t q = t.recip ? quant1<true>(xb, t) : quant1<false>(xb, t);
+        st_global<uint8_t>(qrow + (uint64_t)(c + e), (uint8_t)q);
+      }
+  }
+  if (l == 0) st_global<float>(a.s + (uint64_t)i * (uint64_t)a.s_stride + 4ull * b, t.s);
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(const ActArgs &a, bool fast, hipStream_t stream) {
+  if (a.n_blocks == 0) return hipSuccess;
+  const dim3 grid((a.n_blocks + kActBlocksPerWG - 1) / kActBlocksPerWG);
+  if (fast)
+    hipLaunchKernelGGL(act_quant_kernel<true>, grid, dim3(kActThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(act_quant_kernel<false>, grid, dim3(kActThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace wt

@@ -31,6 +31,7 @@ hipError_t launch_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, uin
                                   hipStream_t stream);
 hipError_t launch_cast_range(uint32_t first, uint64_t count, uint8_t *out, hipStream_t stream);
 hipError_t launch_progress_begin(uint64_t *epoch, hipStream_t stream);
+hipError_t launch_act_quant(const ActArgs &a, bool fast, hipStream_t stream);
 hipError_t launch_progress_mark(const uint64_t *epoch, uint64_t *word, hipStream_t stream);
 }  // namespace wt
 
@@ -557,6 +558,46 @@ wt_status wt_plan_set_progress(wt_plan *plan, uint64_t *words, size_t n_words) {
 wt_status wt_plan_task_unit(const wt_plan *plan, size_t task, int32_t *unit) {
   if (!plan || !unit || task >= plan->L.task_unit.size()) return WT_E_INVAL;
   *unit = plan->L.task_unit[task];
+  return WT_OK;
+}
+
+wt_status wt_quantize_act_b128(const void *x, int64_t n_rows, int64_t cols, int64_t x_row_stride,
+                               const int32_t *row_index, int64_t n_out, void *q, int64_t q_row_stride,
+                               void *scales, int64_t scale_row_stride, void *stream) {
+  auto bad = [](const char *m, wt_status st = WT_E_INVAL) {
+    set_err(nullptr, std::string("wt_quantize_act_b128: ") + m);
+    return st;
+  };
+  if (n_rows < 0 || n_out < 0) return bad("negative row count");
+  if (cols < 1 || cols >= ((int64_t)1 << 31)) return bad("cols out of range");
+  const int64_t nb = (cols + 127) / 128;
+  if (x_row_stride < cols || q_row_stride < cols || scale_row_stride < 4 * nb) return bad("row stride too small");
+  if (n_out == 0) return WT_OK;
+  if (n_out > (((int64_t)1 << 31) - 1) / nb) return bad("n_out * ceil(cols / 128) >= 2^31");
+  if (!q || !scales || (n_rows > 0 && !x)) return bad("NULL pointer");
+  if (n_rows > 0 && (uint64_t)(n_rows - 1) > (UINT64_MAX / 2 - (uint64_t)cols) / (uint64_t)x_row_stride)
+    return bad("x extent overflows");
+  if ((uintptr_t)x % 2) return bad("x not 2-byte aligned", WT_E_ALIGN);
+  if ((uintptr_t)scales % 4 || scale_row_stride % 4) return bad("scales not 4-byte aligned", WT_E_ALIGN);
+  ActArgs a{};
+  a.x = (uint64_t)(uintptr_t)x;
+  a.index = (uint64_t)(uintptr_t)row_index;
+  a.q = (uint64_t)(uintptr_t)q;
+  a.s = (uint64_t)(uintptr_t)scales;
+  a.n_rows = n_rows;
+  a.cols = cols;
+  a.x_stride = x_row_stride;
+  a.q_stride = q_row_stride;
+  a.s_stride = scale_row_stride;
+  a.nb = (uint32_t)nb;
+  a.n_blocks = (uint32_t)(n_out * nb);
+  const bool fast = cols % 8 == 0 && x_row_stride % 8 == 0 && q_row_stride % 8 == 0 && (uintptr_t)x % 16 == 0 &&
+                    (uintptr_t)q % 8 == 0;
+  const hipError_t e = launch_act_quant(a, fast, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_err(nullptr, hip_msg("wt_quantize_act_b128 launch", e));
+    return WT_E_HIP;
+  }
   return WT_OK;
 }
 

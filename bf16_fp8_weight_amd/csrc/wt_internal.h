@@ -83,4 +83,19 @@ struct LaunchTables {
   uint32_t n_copies;
 };
 
+// Arguments of the block-scaled activation quantization (one launch).
+struct ActArgs {
+  uint64_t x;         // BF16 rows, x_stride elements apart
+  uint64_t index;     // int32 output-row -> input-row map, or 0
+  uint64_t q;         // FP8 rows, q_stride bytes apart
+  uint64_t s;         // fp32 scale rows, s_stride bytes apart
+  int64_t n_rows;
+  int64_t cols;
+  int64_t x_stride;
+  int64_t q_stride;
+  int64_t s_stride;
+  uint32_t nb;        // blocks per row, ceil(cols / 128)
+  uint32_t n_blocks;  // n_out * nb < 2^31
+};
+
 }  // namespace wt

@@ -414,6 +414,87 @@ def mla_many_small(device="cpu", materialize=True, layers=8, n_small=4000, host=
     return wl
 
 
+# ------------------------------------------------------- token activations
+@dataclass
+class ActWorkload:
+    """Token activations for block-scaled FP8 quantization (dispatch sender).
+
+    x: [tokens, hidden] BF16. index: int32 output-row -> token map (None: row
+    i is token i). Outputs: n_out rows; with `interleaved` each row is one
+    send-buffer slot of `slot` bytes holding the row's FP8 codes then its
+    scales, else codes and scales are separate dense arrays."""
+
+    name: str
+    tokens: int
+    hidden: int
+    x: Optional[torch.Tensor]
+    index: Optional[torch.Tensor]
+    n_out: int
+    interleaved: bool
+    seed: int
+
+    @property
+    def nb(self) -> int:
+        return ceil_div(self.hidden, TILE)
+
+    @property
+    def q_stride(self) -> int:
+        return self.slot if self.interleaved else self.hidden
+
+    @property
+    def s_stride(self) -> int:
+        return self.slot if self.interleaved else 4 * self.nb
+
+    @property
+    def slot(self) -> int:
+        return align_up(self.hidden + 4 * self.nb, 16)
+
+    @property
+    def input_bytes(self) -> int:
+        return 2 * self.n_out * self.hidden
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Per output row: its BF16 token read, FP8 codes and scales written,
+        plus its 4-byte index when rows are gathered."""
+        return self.n_out * (3 * self.hidden + 4 * self.nb + (4 if self.index is not None else 0))
+
+
+def _activations(shape, g, device, outlier_channels=8) -> torch.Tensor:
+    """Student-t(3) values of unit scale with a few outlier channels x50 (the
+    heavy-tailed, channel-outlier shape of transformer hidden states)."""
+    t = _student_t3_bf16(shape, g, device, scale=1.0).float()
+    ch = torch.randint(0, shape[1], (outlier_channels,), generator=g, device=device)
+    t[:, ch] *= 50.0
+    return t.to(torch.bfloat16)
+
+
+def act_dispatch(device="cpu", tokens=128, hidden=7168, topk=8, n_experts=384, seed=2001,
+                 interleaved=True, materialize=True) -> ActWorkload:
+    """MoE dispatch sender: each token goes to topk distinct experts drawn
+    uniformly; output rows are (token, expert) pairs grouped by expert, so a
+    token's activations appear topk times, each copy quantized into its slot."""
+    g = _gen(device, seed)
+    x = idx = None
+    if materialize:
+        x = _activations((tokens, hidden), g, device)
+        experts = torch.rand((tokens, n_experts), generator=g, device=device).topk(topk, dim=1).indices
+        order = torch.sort(experts.flatten(), stable=True).indices
+        idx = (order // topk).to(torch.int32)
+    wl = ActWorkload(f"act_dispatch_t{tokens}_top{topk}_h{hidden}", tokens, hidden, x, idx, tokens * topk,
+                     interleaved, seed)
+    if not materialize:
+        wl.index = torch.empty(0, dtype=torch.int32)  # marks a gathered workload
+    return wl
+
+
+def act_tokens(device="cpu", tokens=4096, hidden=7168, seed=2002, materialize=True) -> ActWorkload:
+    """A plain batch of tokens (no gather), codes and scales in separate arrays."""
+    g = _gen(device, seed)
+    x = _activations((tokens, hidden), g, device) if materialize else None
+    return ActWorkload(f"act_tokens_t{tokens}_h{hidden}", tokens, hidden, x, None, tokens, False, seed)
+
+
 WORKLOADS = {
     "dense_layer_h1024": dense_layer_h1024,
     "dense_7b": dense_7b,

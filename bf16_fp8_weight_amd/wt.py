@@ -30,7 +30,7 @@ EXPORTS = [
     "wt_plan_get_info", "wt_plan_destroy", "wt_status_str", "wt_plan_last_error",
     "wt_quantize_domain", "wt_cast_f32_range",
     "wt_schedule_build", "wt_schedule_info", "wt_schedule_output", "wt_schedule_tasks", "wt_schedule_destroy",
-    "wt_plan_set_progress", "wt_plan_task_unit", "wt_progress_wait",
+    "wt_plan_set_progress", "wt_plan_task_unit", "wt_progress_wait", "wt_quantize_act_b128",
 ]
 
 
@@ -151,6 +151,8 @@ def _load() -> ctypes.CDLL:
     L.wt_plan_set_progress.argtypes = [vp, vp, sz]
     L.wt_plan_task_unit.restype = ctypes.c_int
     L.wt_plan_task_unit.argtypes = [vp, sz, P(i32)]
+    L.wt_quantize_act_b128.restype = ctypes.c_int
+    L.wt_quantize_act_b128.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     L.wt_progress_wait.restype = ctypes.c_int
     L.wt_progress_wait.argtypes = [vp, ctypes.c_uint64, ctypes.c_uint64]
     return L
@@ -269,6 +271,13 @@ def wt_progress_wait(word: int, target: int, timeout_ns: int) -> bool:
         return False
     _check(st)
     return True
+
+
+def wt_quantize_act_b128(x: int, n_rows: int, cols: int, x_row_stride: int, row_index: int, n_out: int, q: int,
+                         q_row_stride: int, scales: int, scale_row_stride: int, stream: int = 0) -> None:
+    """Addresses as integers (0 = NULL); see include/wt.h."""
+    _check(lib.wt_quantize_act_b128(x or None, n_rows, cols, x_row_stride, row_index or None, n_out, q or None,
+                                    q_row_stride, scales or None, scale_row_stride, stream or None))
 
 
 def wt_plan_destroy(plan: int) -> None:

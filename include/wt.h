@@ -285,6 +285,43 @@ wt_status wt_schedule_tasks(const wt_schedule *sch, int32_t source, wt_task *tas
 /* Frees the schedule. NULL is ignored. */
 void wt_schedule_destroy(wt_schedule *sch);
 
+/* ---- Block-scaled FP8 quantization of token activations ----
+ * The sender half of MoE dispatch quantizes token activations to FP8 with
+ * block scales before writing them to peers ("Enabling trillion-parameter
+ * models on AWS EFA", dispatch/combine evaluation: hidden size 7168, FP8
+ * dispatch with block scales; the sender shuffles tokens into send buffers
+ * so each peer receives one write). Blocks are 1 x 128: one token's 128
+ * consecutive channels, the last block of a row holding cols % 128 channels
+ * when cols is not a multiple of 128. Per block s = amax / 448 in IEEE fp32
+ * (1 for an all-zero block) and q = E4M3(fl32(x / s)), round to nearest even,
+ * saturating: the same arithmetic as the weight tiles.
+ *
+ * x: n_rows rows of BF16 on the device, x_row_stride elements apart (>= cols),
+ *    2-byte aligned.
+ * row_index: NULL, or n_out int32 input-row indices on the device: output
+ *    row i quantizes input row row_index[i] (row i when NULL). Output rows
+ *    whose index is outside [0, n_rows) are not written. Indices may repeat.
+ * q: n_out rows of q_row_stride bytes (>= cols), device or pinned host; the
+ *    first cols bytes of a row receive the FP8 codes, the rest is untouched.
+ * scales: n_out rows of scale_row_stride bytes (>= 4 ceil(cols / 128)),
+ *    4-byte aligned, device or pinned host; the row's block scales as fp32.
+ *    q and scales may interleave (e.g. one send-buffer slot per token holding
+ *    its codes, then its scales) as long as no two written ranges overlap.
+ * Shapes with cols, x_row_stride and q_row_stride multiples of 8, x 16-byte
+ * and q 8-byte aligned take the vector path; any other shape takes a general
+ * path with the same results.
+ * Enqueued on `stream` (a hipStream_t; NULL = the default stream); returns
+ * without waiting. Errors: WT_E_INVAL for negative or inconsistent sizes,
+ * NULL pointers with n_out > 0, n_out * ceil(cols / 128) >= 2^31 or
+ * cols >= 2^31; WT_E_ALIGN for a misaligned x or scales; WT_E_HIP if the
+ * launch fails. Pointer kinds and extents are not queried (that would cost a
+ * runtime call per pointer per call on the dispatch path): the caller
+ * guarantees that every range above lies in its allocation. n_out == 0 is a
+ * no-op. */
+wt_status wt_quantize_act_b128(const void *x, int64_t n_rows, int64_t cols, int64_t x_row_stride,
+                               const int32_t *row_index, int64_t n_out, void *q, int64_t q_row_stride,
+                               void *scales, int64_t scale_row_stride, void *stream);
+
 /* ---- Completion counters ----
  * Host-visible words that the GPU writes as parts of a replay finish, so a
  * host thread can start moving a part of the destination region (the one-sided
