@@ -21,8 +21,15 @@
 namespace wt {
 namespace {
 
-constexpr int kActThreads = 256;
-constexpr int kActBlocksPerWG = kActThreads / 16;
+#ifndef WT_ACT_THREADS
+#define WT_ACT_THREADS 256
+#endif
+#ifndef WT_ACT_K
+#define WT_ACT_K 1
+#endif
+constexpr int kActThreads = WT_ACT_THREADS;
+constexpr int kActGroups = kActThreads / 16;  // 16-lane groups per workgroup
+constexpr int kActK = WT_ACT_K;               // blocks per group (loads in flight per lane)
 
 __device__ __forceinline__ uint32_t row16_max(uint32_t m) {
   m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x0B1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
@@ -37,64 +44,87 @@ __device__ __forceinline__ uint2 quant8(const uint32_t w[4], const TileQ &t) {
   return make_uint2(quant4<Recip>(w[0], w[1], t), quant4<Recip>(w[2], w[3], t));
 }
 
+// Where block gblk of the launch lives: its output row, block column and
+// source row; has = this lane holds channels of it.
+struct BlockAt {
+  uint32_t i, b;
+  int64_t src, c;
+  bool has;
+};
+
+__device__ __forceinline__ BlockAt locate(const ActArgs &a, uint32_t gblk, uint32_t l) {
+  BlockAt p{0, 0, -1, 0, false};
+  if (gblk < a.n_blocks) {
+    p.i = gblk / a.nb;
+    p.b = gblk - p.i * a.nb;
+    p.src = a.index ? (int64_t)ld_global<int32_t>(a.index + 4ull * p.i) : (int64_t)p.i;
+    p.c = 128 * (int64_t)p.b + 8 * (int64_t)l;
+    p.has = p.src >= 0 && p.src < a.n_rows && p.c < a.cols;
+  }
+  return p;
+}
+
 // Fast: cols, x_stride, q_stride multiples of 8, x 16-byte and q 8-byte
-// aligned. General: any shape and alignment (2-byte loads, byte stores).
-template <bool Fast>
+// aligned; each group takes K blocks, all K loads issued before any use.
+// General (K = 1): any shape and alignment (2-byte loads, byte stores).
+template <bool Fast, int K>
 __global__ void __launch_bounds__(kActThreads) act_quant_kernel(ActArgs a) {
-  const uint32_t gblk = blockIdx.x * (uint32_t)kActBlocksPerWG + (threadIdx.x >> 4);
   const uint32_t l = threadIdx.x & 15;
-  bool valid = gblk < a.n_blocks;
-  uint32_t i = 0, b = 0;
-  int64_t src = -1;
-  if (valid) {
-    i = gblk / a.nb;
-    b = gblk - i * a.nb;
-    src = a.index ? (int64_t)ld_global<int32_t>(a.index + 4ull * i) : (int64_t)i;
-    valid = src >= 0 && src < a.n_rows;
-  }
-  const int64_t c = 128 * (int64_t)b + 8 * (int64_t)l;
-  const bool has = valid && c < a.cols;
-  const uint64_t xrow = a.x + 2ull * (uint64_t)src * (uint64_t)a.x_stride;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  if (Fast) {
-    if (has) {
-      const uint4 v = ld_global<uint4>(xrow + 2ull * (uint64_t)c);
-      w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
-    }
-  } else if (has) {
+  const uint32_t base = blockIdx.x * (uint32_t)(kActGroups * K) + (threadIdx.x >> 4);
+  BlockAt p[K];
+  uint32_t w[K][4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (c + e < a.cols) w[e >> 1] |= (uint32_t)ld_global<uint16_t>(xrow + 2ull * (uint64_t)(c + e)) << (16 * (e & 1));
-  }
-  uint32_t m = pk_max_u16(pk_max_u16(abs2(w[0]), abs2(w[1])), pk_max_u16(abs2(w[2]), abs2(w[3])));
-  m = row16_max(max(m & 0xFFFFu, m >> 16));  // every lane of the row takes part
-  if (!has) return;
-  const TileQ t = block_quant(m);
-  const uint64_t qrow = a.q + (uint64_t)i * (uint64_t)a.q_stride;
-  if (Fast) {
-    const uint2 q = t.recip ? quant8<true>(w, t) : quant8<false>(w, t);
-    st_global<uint2>(qrow + (uint64_t)c, q);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (c + e < a.cols) {
-        const uint32_t xb = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t q = t.recip ? quant1<true>(xb, t) : quant1<false>(xb, t);
-        st_global<uint8_t>(qrow + (uint64_t)(c + e), (uint8_t)q);
+  for (int k = 0; k < K; ++k) {
+    p[k] = locate(a, base + (uint32_t)(k * kActGroups), l);
+    w[k][0] = w[k][1] = w[k][2] = w[k][3] = 0u;
+    const uint64_t xrow = a.x + 2ull * (uint64_t)p[k].src * (uint64_t)a.x_stride;
+    if (Fast) {
+      if (p[k].has) {
+        const uint4 v = ld_global<uint4>(xrow + 2ull * (uint64_t)p[k].c);
+        w[k][0] = v.x, w[k][1] = v.y, w[k][2] = v.z, w[k][3] = v.w;
       }
+    } else if (p[k].has) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (p[k].c + e < a.cols)
+          w[k][e >> 1] |= (uint32_t)ld_global<uint16_t>(xrow + 2ull * (uint64_t)(p[k].c + e)) << (16 * (e & 1));
+    }
   }
-  if (l == 0) st_global<float>(a.s + (uint64_t)i * (uint64_t)a.s_stride + 4ull * b, t.s);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    uint32_t m = pk_max_u16(pk_max_u16(abs2(w[k][0]), abs2(w[k][1])), pk_max_u16(abs2(w[k][2]), abs2(w[k][3])));
+    m = row16_max(max(m & 0xFFFFu, m >> 16));  // every lane of the row takes part
+    if (p[k].has) {
+      const TileQ t = block_quant(m);
+      const uint64_t qrow = a.q + (uint64_t)p[k].i * (uint64_t)a.q_stride;
+      if (Fast) {
+        const uint2 q = t.recip ? quant8<true>(w[k], t) : quant8<false>(w[k], t);
+        st_global<uint2>(qrow + (uint64_t)p[k].c, q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (p[k].c + e < a.cols) {
+            const uint32_t xb = (w[k][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t q = t.recip ? quant1<true>(xb, t) : quant1<false>(xb, t);
+            st_global<uint8_t>(qrow + (uint64_t)(p[k].c + e), (uint8_t)q);
+          }
+      }
+      if (l == 0) st_global<float>(a.s + (uint64_t)p[k].i * (uint64_t)a.s_stride + 4ull * p[k].b, t.s);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_act_quant(const ActArgs &a, bool fast, hipStream_t stream) {
   if (a.n_blocks == 0) return hipSuccess;
-  const dim3 grid((a.n_blocks + kActBlocksPerWG - 1) / kActBlocksPerWG);
-  if (fast)
-    hipLaunchKernelGGL(act_quant_kernel<true>, grid, dim3(kActThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(act_quant_kernel<false>, grid, dim3(kActThreads), 0, stream, a);
+  if (fast) {
+    const dim3 grid((a.n_blocks + kActGroups * kActK - 1) / (kActGroups * kActK));
+    hipLaunchKernelGGL((act_quant_kernel<true, kActK>), grid, dim3(kActThreads), 0, stream, a);
+  } else {
+    const dim3 grid((a.n_blocks + kActGroups - 1) / kActGroups);
+    hipLaunchKernelGGL((act_quant_kernel<false, 1>), grid, dim3(kActThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
