@@ -42,6 +42,7 @@ def main() -> int:
     ap.add_argument("--dst-kind", default="device", choices=["device", "pinned"],
                     help="destination region in device memory or pinned host memory")
     ap.add_argument("--watermark-mb", type=int, default=0, help="pipeline watermark (0 = library default)")
+    ap.add_argument("--load-hint", type=int, default=0, help="wt_plan_options.load_hint (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the workload, time a plain device-to-device copy of BYTES (counter calibration)")
@@ -83,6 +84,7 @@ def main() -> int:
     opts.dst_write_mode = wt.WT_DST_STAGED if args.dst_mode == "staged" else wt.WT_DST_ZERO_COPY
     if args.watermark_mb:
         opts.watermark_bytes = args.watermark_mb << 20
+    opts.load_hint = args.load_hint
     plan = wt.Plan(wl, dst, dst_kind, opts)
     info = plan.info()
     log(f"plan: {info}")
@@ -256,13 +258,9 @@ def _copy_calibration(nbytes: int, steps: int, warmup: int) -> int:
 
 
 def _kernel_sha() -> str:
-    import hashlib
+    from bf16_fp8_weight_amd.traffic import kernel_sha
 
-    h = hashlib.sha256()
-    for f in ("prep_kernels.hip", "wt_internal.h"):
-        with open(os.path.join(ROOT, "bf16_fp8_weight_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    return kernel_sha()
 
 
 def _cpu_baseline(wl, dst, threads):

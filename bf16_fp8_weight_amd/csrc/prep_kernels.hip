@@ -95,17 +95,40 @@ __device__ __forceinline__ uint32_t chunk_off(int k, uint32_t C) {
   return (c >> 4) * C + (c & 15) * 8;
 }
 
+// A regular tile's loads, plain or non-temporal (RegDesc flag kRegStream,
+// chosen per output at plan time; the data is never reused either way).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool Stream>
+__device__ __forceinline__ uint4 ld_tile(uint64_t a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (Stream) {
+    const u32x4_t v = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t *)(uintptr_t)a);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+#endif
+  return ld_global<uint4>(a);
+}
+
+template <bool Stream>
+__device__ __forceinline__ void load_reg_tile(const RegDesc &x, uint4 (&v)[CH]) {
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    v[k] = ld_tile<Stream>(x.src + 2 * chunk_off(k, x.C));
+    pace_loads(k);
+  }
+}
+
 // Regular tile: a full 128 x 128 tile whose rows all come from one shard,
 // addresses resolved at plan time (one scalar load of its descriptor); every
 // chunk is loaded and stored unconditionally.
 __device__ __forceinline__ void reg_tile(const LaunchTables &T, uint32_t b, uint32_t *red) {
   const RegDesc x = ld_table(T.fast_tiles, b);
   uint4 v[CH];
-#pragma unroll
-  for (int k = 0; k < CH; ++k) {
-    v[k] = ld_global<uint4>(x.src + 2 * chunk_off(k, x.C));
-    pace_loads(k);
-  }
+  if (x.flags & kRegStream)
+    load_reg_tile<true>(x, v);
+  else
+    load_reg_tile<false>(x, v);
   const TileQ t = tile_quant(block_max<TW>(amax_chunks(v), red));
   if (t.recip) {
 #pragma unroll

@@ -54,9 +54,10 @@ struct RegDesc {
   uint64_t q;    // FP8 address of the tile's element (0, 0)
   uint64_t s;    // address of the tile's scale
   uint32_t C;    // row length in elements (< 2^24)
-  uint32_t pad;
+  uint32_t flags;  // kRegStream: read with non-temporal loads
 };
 static_assert(sizeof(RegDesc) == 32, "RegDesc layout");
+constexpr uint32_t kRegStream = 1;
 
 // One byte-range copy (BF16 pass-through). width = 16, 4 or 2: src, dst and
 // bytes are all multiples of width.

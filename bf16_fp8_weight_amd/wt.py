@@ -24,6 +24,7 @@ WT_MEM_DEVICE = 0
 WT_MEM_PINNED_HOST = 1
 WT_DST_ZERO_COPY = 0
 WT_DST_STAGED = 1
+WT_LOAD_AUTO, WT_LOAD_PLAIN, WT_LOAD_STREAM = range(3)
 
 EXPORTS = [
     "wt_plan_options_init", "wt_plan_check", "wt_plan_schedule", "wt_plan_create", "wt_prepare",
@@ -57,7 +58,8 @@ class wt_plan_options(ctypes.Structure):
         ("chunk_bytes", ctypes.c_uint64),
         ("dst_write_mode", ctypes.c_int32),
         ("device", ctypes.c_int32),
-        ("reserved", ctypes.c_uint32 * 6),
+        ("load_hint", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32 * 5),
     ]
 
 

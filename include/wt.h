@@ -110,8 +110,15 @@ typedef struct wt_plan_options {
   uint64_t chunk_bytes;
   int32_t dst_write_mode; /* WT_DST_ZERO_COPY (default) or WT_DST_STAGED */
   int32_t device;         /* HIP device ordinal; -1 (default) = current device */
-  uint32_t reserved[6];
+  /* Cache hint for reading full 128 x 128 tiles: WT_LOAD_AUTO (default; the
+   * library's choice, currently plain loads), WT_LOAD_PLAIN, or
+   * WT_LOAD_STREAM (non-temporal loads). Affects speed only, never results;
+   * values above WT_LOAD_STREAM are WT_E_INVAL. */
+  uint32_t load_hint;
+  uint32_t reserved[5];
 } wt_plan_options;
+
+enum { WT_LOAD_AUTO = 0, WT_LOAD_PLAIN = 1, WT_LOAD_STREAM = 2 };
 
 /* Shape of a plan, filled by wt_plan_check / wt_plan_get_info. */
 typedef struct wt_plan_info {

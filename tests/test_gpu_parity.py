@@ -35,6 +35,16 @@ def test_dense_layer_h1024():
     assert info["n_launches"] == 1
 
 
+@pytest.mark.parametrize("hint", [1, 2])
+def test_load_hints_same_bytes(hint):
+    from bf16_fp8_weight_amd import wt
+
+    wl = W.custom([(512, 2048), (384, 7168), (256, 4096)], n_shards=2, device="cuda")
+    o = wt.wt_plan_options_init()
+    o.load_hint = hint
+    _parity(wl, opts=o)
+
+
 def test_ragged_stress_reduced():
     wl = W.ragged_stress(device="cuda", n_tensors=40, max_dim=1400)
     _parity(wl)

@@ -93,6 +93,16 @@ def test_validation_errors(wt):
     assert "watermark" in wt.wt_plan_last_error(None)
 
 
+def test_load_hint_range(wt):
+    o = wt.wt_plan_options_init()
+    assert o.load_hint == wt.WT_LOAD_AUTO
+    for h in range(3):
+        o.load_hint = h
+        assert _status(wt, [_one(wt)], opts=o) == 0
+    o.load_hint = 3
+    assert _status(wt, [_one(wt)], opts=o) == wt.WT_E_INVAL
+
+
 def test_fused_group_offsets_from_first_task(wt):
     # the second member's offsets are ignored, so they may be anything
     ok = [_one(wt, fusion_group=1, scale_offset=1024), _one(wt, fusion_group=1, dst_offset=10 ** 9, scale_offset=10 ** 9)]
