@@ -347,11 +347,11 @@ wt_status build_layout(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, i
 }
 
 // Whether full tiles are read with non-temporal loads. Measured on MI355X
-// (ms per launch, plain vs streaming): Kimi-K2-shaped MoE share 2.10 vs 2.07,
-// 7B-shaped dense model 3.43 vs 3.54, MLA attention stack 0.474 vs 0.477,
-// hidden-1024 layer 0.0097 vs 0.0105; per-row-length rules (streaming only
-// power-of-two row strides, or only the others) helped neither. So the
-// default is plain loads.
+// with non-temporal stores, ms per launch, plain vs streaming loads:
+// Kimi-K2-shaped MoE share 2.075 vs 2.146, 7B-shaped dense model 3.266 vs
+// 3.245, MLA attention stack 0.459 vs 0.450; streaming only the outputs with
+// power-of-two row strides, or only the others, helped none of them. The
+// default is plain loads, the better choice on the MoE share.
 static bool stream_loads(uint32_t hint) { return hint == WT_LOAD_STREAM; }
 
 void build_tables(const Layout &L, const std::vector<int32_t> &outputs, const BatchAddr &addr, HostTables *t) {

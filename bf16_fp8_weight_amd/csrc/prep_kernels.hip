@@ -110,6 +110,38 @@ __device__ __forceinline__ uint4 ld_tile(uint64_t a) {
   return ld_global<uint4>(a);
 }
 
+// Stores of prepared bytes (tiles and pass-through copies): written once and
+// never read back here, so they carry the non-temporal hint. Measured on
+// MI355X, ms per launch with plain vs non-temporal stores: Kimi-K2-shaped MoE
+// share 2.114 vs 2.075, 7B-shaped dense model 3.423 vs 3.266, MLA attention
+// stack 0.470 vs 0.459; the ragged set (mostly general tiles, whose byte
+// stores stay plain) 1.061 vs 1.092.
+#ifndef WT_NT_STORE
+#define WT_NT_STORE 1
+#endif
+template <class T>
+__device__ __forceinline__ void st_stream(uint64_t a, const T &v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (WT_NT_STORE) {
+    __builtin_nontemporal_store(v, (__attribute__((address_space(1))) T *)(uintptr_t)a);
+    return;
+  }
+#endif
+  st_global<T>(a, v);
+}
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_q8(uint64_t a, uint2 q) {
+  u32x2_t v;
+  v.x = q.x;
+  v.y = q.y;
+  st_stream<u32x2_t>(a, v);
+}
+__device__ __forceinline__ void st_q16(uint64_t a, const uint4 &q) {
+  u32x4_t v;
+  v.x = q.x, v.y = q.y, v.z = q.z, v.w = q.w;
+  st_stream<u32x4_t>(a, v);
+}
+
 template <bool Stream>
 __device__ __forceinline__ void load_reg_tile(const RegDesc &x, uint4 (&v)[CH]) {
 #pragma unroll
@@ -136,7 +168,7 @@ __device__ __forceinline__ void reg_tile(const LaunchTables &T, uint32_t b, uint
       uint2 q;
       q.x = quant4<true>(v[k].x, v[k].y, t);
       q.y = quant4<true>(v[k].z, v[k].w, t);
-      st_global<uint2>(x.q + chunk_off(k, x.C), q);
+      st_q8(x.q + chunk_off(k, x.C), q);
     }
   } else {
 #pragma unroll
@@ -144,7 +176,7 @@ __device__ __forceinline__ void reg_tile(const LaunchTables &T, uint32_t b, uint
       uint2 q;
       q.x = quant4<false>(v[k].x, v[k].y, t);
       q.y = quant4<false>(v[k].z, v[k].w, t);
-      st_global<uint2>(x.q + chunk_off(k, x.C), q);
+      st_q8(x.q + chunk_off(k, x.C), q);
     }
   }
   if (threadIdx.x == 0) st_global<float>(x.s, t.s);
@@ -164,7 +196,7 @@ __device__ __forceinline__ void edge_store(const uint4 (&v)[CH], uint64_t qbase,
       uint2 q;
       q.x = quant4<Recip>(v[k].x, v[k].y, t);
       q.y = quant4<Recip>(v[k].z, v[k].w, t);
-      st_global<uint2>(qbase + chunk_off(k, C), q);
+      st_q8(qbase + chunk_off(k, C), q);
     }
   }
 }
@@ -222,16 +254,16 @@ __device__ __forceinline__ void edge_tile(const LaunchTables &T, uint32_t b, uin
 __device__ __forceinline__ void copy_item(const CopyItem ci, int lane) {
   switch (ci.width) {
     case 16:
-      for (uint32_t i = lane; i < ci.bytes / 16; i += 64) st_global(ci.dst + 16ull * i, ld_global<uint4>(ci.src + 16ull * i));
+      for (uint32_t i = lane; i < ci.bytes / 16; i += 64) st_q16(ci.dst + 16ull * i, ld_global<uint4>(ci.src + 16ull * i));
       break;
     case 4:
-      for (uint32_t i = lane; i < ci.bytes / 4; i += 64) st_global(ci.dst + 4ull * i, ld_global<uint32_t>(ci.src + 4ull * i));
+      for (uint32_t i = lane; i < ci.bytes / 4; i += 64) st_stream<uint32_t>(ci.dst + 4ull * i, ld_global<uint32_t>(ci.src + 4ull * i));
       break;
     case 2:
-      for (uint32_t i = lane; i < ci.bytes / 2; i += 64) st_global(ci.dst + 2ull * i, ld_global<uint16_t>(ci.src + 2ull * i));
+      for (uint32_t i = lane; i < ci.bytes / 2; i += 64) st_stream<uint16_t>(ci.dst + 2ull * i, ld_global<uint16_t>(ci.src + 2ull * i));
       break;
     default:
-      for (uint32_t i = lane; i < ci.bytes; i += 64) st_global(ci.dst + i, ld_global<uint8_t>(ci.src + i));
+      for (uint32_t i = lane; i < ci.bytes; i += 64) st_stream<uint8_t>(ci.dst + i, ld_global<uint8_t>(ci.src + i));
       break;
   }
 }
