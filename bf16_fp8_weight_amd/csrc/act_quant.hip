@@ -27,6 +27,40 @@ namespace {
 #ifndef WT_ACT_K
 #define WT_ACT_K 1
 #endif
+// Cache hints, measured on MI355X for 4096 x 7168 (us per launch, back to
+// back): plain 16.47, non-temporal stores 16.94, non-temporal loads 18.84,
+// both 17.52. Plain accesses stay the default.
+#ifndef WT_ACT_NT_LOAD
+#define WT_ACT_NT_LOAD 0
+#endif
+#ifndef WT_ACT_NT_STORE
+#define WT_ACT_NT_STORE 0
+#endif
+typedef unsigned int act_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int act_u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 act_load16(uint64_t a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (WT_ACT_NT_LOAD) {
+    const act_u32x4 v = __builtin_nontemporal_load((const __attribute__((address_space(1))) act_u32x4 *)(uintptr_t)a);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+#endif
+  return ld_global<uint4>(a);
+}
+
+__device__ __forceinline__ void act_store8(uint64_t a, uint2 q) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (WT_ACT_NT_STORE) {
+    act_u32x2 v;
+    v.x = q.x;
+    v.y = q.y;
+    __builtin_nontemporal_store(v, (__attribute__((address_space(1))) act_u32x2 *)(uintptr_t)a);
+    return;
+  }
+#endif
+  st_global<uint2>(a, q);
+}
 constexpr int kActThreads = WT_ACT_THREADS;
 constexpr int kActGroups = kActThreads / 16;  // 16-lane groups per workgroup
 constexpr int kActK = WT_ACT_K;               // blocks per group (loads in flight per lane)
@@ -80,7 +114,7 @@ __global__ void __launch_bounds__(kActThreads) act_quant_kernel(ActArgs a) {
     const uint64_t xrow = a.x + 2ull * (uint64_t)p[k].src * (uint64_t)a.x_stride;
     if (Fast) {
       if (p[k].has) {
-        const uint4 v = ld_global<uint4>(xrow + 2ull * (uint64_t)p[k].c);
+        const uint4 v = act_load16(xrow + 2ull * (uint64_t)p[k].c);
         w[k][0] = v.x, w[k][1] = v.y, w[k][2] = v.z, w[k][3] = v.w;
       }
     } else if (p[k].has) {
@@ -99,7 +133,7 @@ __global__ void __launch_bounds__(kActThreads) act_quant_kernel(ActArgs a) {
       const uint64_t qrow = a.q + (uint64_t)p[k].i * (uint64_t)a.q_stride;
       if (Fast) {
         const uint2 q = t.recip ? quant8<true>(w[k], t) : quant8<false>(w[k], t);
-        st_global<uint2>(qrow + (uint64_t)p[k].c, q);
+        act_store8(qrow + (uint64_t)p[k].c, q);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
