@@ -346,13 +346,15 @@ wt_status build_layout(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, i
   return WT_OK;
 }
 
+
+
 // Whether full tiles are read with non-temporal loads. Measured on MI355X
-// with non-temporal stores, ms per launch, plain vs streaming loads:
-// Kimi-K2-shaped MoE share 2.075 vs 2.146, 7B-shaped dense model 3.266 vs
-// 3.245, MLA attention stack 0.459 vs 0.450; streaming only the outputs with
-// power-of-two row strides, or only the others, helped none of them. The
-// default is plain loads, the better choice on the MoE share.
-static bool stream_loads(uint32_t hint) { return hint == WT_LOAD_STREAM; }
+// with tile pairs and non-temporal stores, ms per launch, plain vs streaming
+// loads: Kimi-K2-shaped MoE share 2.050 vs 2.015, 7B-shaped dense model 3.165
+// vs 3.106, MLA attention stack 0.444 vs 0.421. (With one tile per
+// workgroup the MoE share preferred plain loads, 2.075 vs 2.146.) The default
+// streams.
+static bool stream_loads(uint32_t hint) { return hint != WT_LOAD_PLAIN; }
 
 void build_tables(const Layout &L, const std::vector<int32_t> &outputs, const BatchAddr &addr, HostTables *t) {
   *t = HostTables{};
@@ -407,6 +409,14 @@ void build_tables(const Layout &L, const std::vector<int32_t> &outputs, const Ba
           r.s = d.s + 4 * ((uint64_t)I * (uint64_t)H.tiles_c + (uint64_t)J);
           r.C = (uint32_t)H.cols;
           r.flags = stream_loads(L.load_hint) ? kRegStream : 0;
+          // the next tiles of the row band are full too (same rows, same segment): one descriptor for a group
+          if (kGroupTiles >= 4 && (J + 4) * kTile <= H.cols) {
+            r.flags |= kRegQuad;
+            J += 3;
+          } else if (kGroupTiles >= 2 && (J + 2) * kTile <= H.cols) {
+            r.flags |= kRegPair;
+            J += 1;
+          }
           t->fast.push_back(r);
         }
       }

@@ -154,8 +154,7 @@ __device__ __forceinline__ void load_reg_tile(const RegDesc &x, uint4 (&v)[CH]) 
 // Regular tile: a full 128 x 128 tile whose rows all come from one shard,
 // addresses resolved at plan time (one scalar load of its descriptor); every
 // chunk is loaded and stored unconditionally.
-__device__ __forceinline__ void reg_tile(const LaunchTables &T, uint32_t b, uint32_t *red) {
-  const RegDesc x = ld_table(T.fast_tiles, b);
+__device__ __forceinline__ void reg_tile(const RegDesc &x, uint32_t *red) {
   uint4 v[CH];
   if (x.flags & kRegStream)
     load_reg_tile<true>(x, v);
@@ -180,6 +179,80 @@ __device__ __forceinline__ void reg_tile(const LaunchTables &T, uint32_t b, uint
     }
   }
   if (threadIdx.x == 0) st_global<float>(x.s, t.s);
+}
+
+// Group of NJ regular tiles (I, J) .. (I, J + NJ - 1) of one row band (NJ =
+// 2 or 4): rows of 256 NJ bytes (16 NJ chunks); thread t owns chunks
+// t + TT k (k < NJ CH): row (t + TT k) / (16 NJ), chunk t % (16 NJ), so the
+// 16-lane DPP row of lane l holds tile (l / 16) % NJ throughout, and each
+// wave instruction reads 1 KB of complete group rows and writes 512 bytes.
+// The row reduction of the DPP rows therefore yields per-tile maxima.
+template <int NJ, bool Stream>
+__device__ __forceinline__ void load_group(const RegDesc &x, uint4 (&v)[NJ * CH]) {
+#pragma unroll
+  for (int k = 0; k < NJ * CH; ++k) {
+    const uint32_t c = threadIdx.x + TT * k;
+    v[k] = ld_tile<Stream>(x.src + 2 * ((c / (16 * NJ)) * x.C + (c % (16 * NJ)) * 8));
+    pace_loads(k);
+  }
+}
+
+template <int NJ, bool Recip>
+__device__ __forceinline__ void store_group(const RegDesc &x, const uint4 (&v)[NJ * CH], const TileQ &t) {
+#pragma unroll
+  for (int k = 0; k < NJ * CH; ++k) {
+    const uint32_t c = threadIdx.x + TT * k;
+    uint2 q;
+    q.x = quant4<Recip>(v[k].x, v[k].y, t);
+    q.y = quant4<Recip>(v[k].z, v[k].w, t);
+    st_q8(x.q + (c / (16 * NJ)) * x.C + (c % (16 * NJ)) * 8, q);
+  }
+}
+
+template <int NJ>
+__device__ __forceinline__ void group_tile(const RegDesc &x, uint32_t *red) {
+  static_assert(NJ == 2 || NJ == 4, "tiles per group");
+  uint4 v[NJ * CH];
+  if (x.flags & kRegStream)
+    load_group<NJ, true>(x, v);
+  else
+    load_group<NJ, false>(x, v);
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < NJ * CH; ++k) {
+    m = pk_max_u16(m, abs2(v[k].x));
+    m = pk_max_u16(m, abs2(v[k].y));
+    m = pk_max_u16(m, abs2(v[k].z));
+    m = pk_max_u16(m, abs2(v[k].w));
+  }
+  m = max(m & 0xFFFFu, m >> 16);
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, true));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, true));
+  // lane 15 of DPP row r holds the maximum of tile r % NJ over that row
+  const uint32_t r15 = (uint32_t)__builtin_amdgcn_readlane((int)m, 15), r31 = (uint32_t)__builtin_amdgcn_readlane((int)m, 31);
+  const uint32_t r47 = (uint32_t)__builtin_amdgcn_readlane((int)m, 47), r63 = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
+  if ((threadIdx.x & 63) == 0) {
+    uint32_t *w = red + NJ * (threadIdx.x >> 6);
+    if (NJ == 2) {
+      w[0] = max(r15, r47);
+      w[1] = max(r31, r63);
+    } else {
+      w[0] = r15, w[1] = r31, w[2] = r47, w[3] = r63;
+    }
+  }
+  __syncthreads();
+  const uint32_t tile = (threadIdx.x >> 4) % NJ;  // the tile of this thread's chunks
+  uint32_t a = red[tile];
+#pragma unroll
+  for (int i = 1; i < TW; ++i) a = max(a, red[NJ * i + tile]);
+  const TileQ t = block_quant(a);  // differs between the DPP rows of a wave
+  if (t.recip)
+    store_group<NJ, true>(x, v, t);
+  else
+    store_group<NJ, false>(x, v, t);
+  if (threadIdx.x < 16 * NJ && (threadIdx.x & 15) == 0) st_global<float>(x.s + 4 * tile, t.s);
 }
 
 // Edge tile: partial (last tile row or column of an output), or rows from
@@ -387,10 +460,16 @@ __device__ __forceinline__ void general_tile(const LaunchTables &T, const TileIt
 // edge tile each; then TW copy items per block (one per wave). At most
 // WT_BLOCKS_PER_CU blocks per compute unit (dynamic-LDS request).
 __global__ __launch_bounds__(TT) void prep_fast_copy_kernel(LaunchTables T) {
-  __shared__ uint32_t red[TW];
+  __shared__ uint32_t red[4 * TW];
   uint32_t b = blockIdx.x;
   if (b < T.n_fast) {
-    reg_tile(T, b, red);
+    const RegDesc x = ld_table(T.fast_tiles, b);
+    if (kGroupTiles >= 4 && (x.flags & kRegQuad))
+      group_tile<kGroupTiles >= 4 ? 4 : 2>(x, red);
+    else if (kGroupTiles >= 2 && (x.flags & kRegPair))
+      group_tile<2>(x, red);
+    else
+      reg_tile(x, red);
     return;
   }
   b -= T.n_fast;

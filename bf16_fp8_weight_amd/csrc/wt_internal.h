@@ -58,6 +58,20 @@ struct RegDesc {
 };
 static_assert(sizeof(RegDesc) == 32, "RegDesc layout");
 constexpr uint32_t kRegStream = 1;
+constexpr uint32_t kRegPair = 2;  // the descriptor covers tiles (I, J) and (I, J + 1)
+constexpr uint32_t kRegQuad = 4;  // the descriptor covers tiles (I, J) .. (I, J + 3)
+
+// Up to this many adjacent full tiles of a row band (1, 2 or 4) are prepared
+// by one workgroup; the plan emits groups no larger than this and the kernel
+// compiles only those paths (a larger group needs more registers). Measured
+// on MI355X with streaming loads, ms per launch for 1 / 2 / 4 tiles: Kimi-K2
+// MoE share 2.146 / 2.006 / 2.253, 7B dense 3.245 / 3.097 / 3.387 (four
+// tiles need 94 VGPRs, which caps a compute unit at two workgroups).
+#ifndef WT_GROUP_TILES
+#define WT_GROUP_TILES 2
+#endif
+constexpr int kGroupTiles = WT_GROUP_TILES;
+static_assert(kGroupTiles == 1 || kGroupTiles == 2 || kGroupTiles == 4, "tiles per group");
 
 // One byte-range copy (BF16 pass-through). width = 16, 4 or 2: src, dst and
 // bytes are all multiples of width.

@@ -111,7 +111,7 @@ typedef struct wt_plan_options {
   int32_t dst_write_mode; /* WT_DST_ZERO_COPY (default) or WT_DST_STAGED */
   int32_t device;         /* HIP device ordinal; -1 (default) = current device */
   /* Cache hint for reading full 128 x 128 tiles: WT_LOAD_AUTO (default; the
-   * library's choice, currently plain loads), WT_LOAD_PLAIN, or
+   * library's choice, currently non-temporal loads), WT_LOAD_PLAIN, or
    * WT_LOAD_STREAM (non-temporal loads). Affects speed only, never results;
    * values above WT_LOAD_STREAM are WT_E_INVAL. */
   uint32_t load_hint;

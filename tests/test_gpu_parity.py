@@ -45,6 +45,19 @@ def test_load_hints_same_bytes(hint):
     _parity(wl, opts=o)
 
 
+@pytest.mark.parametrize("hint", [1, 2])
+def test_tile_groups_with_leftovers(hint):
+    # rows of 3 and 5 full tiles: pairs plus a single tile at the end of each band;
+    # 1 and 2 full tiles; a band split across shards (edge tiles) next to paired bands
+    from bf16_fp8_weight_amd import wt
+
+    wl = W.custom([(384, 384), (256, 640), (128, 128), (256, 256), (512, 1152)], n_shards=4, device="cuda",
+                  dist="t")
+    o = wt.wt_plan_options_init()
+    o.load_hint = hint
+    _parity(wl, opts=o)
+
+
 def test_ragged_stress_reduced():
     wl = W.ragged_stress(device="cuda", n_tensors=40, max_dim=1400)
     _parity(wl)
