@@ -178,8 +178,20 @@ wt_status build_layout(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, i
     if (staged) n += H.data_bytes + H.scale_bytes + 4 * (int64_t)kStageAlign;
     return (int64_t)align_up((uint64_t)n, kSlotAlign);
   };
+  // Default chunk size: about kTargetChunks chunks per replay, at least 32 MiB
+  // and at most half the watermark. Measured on MI355X with the pinned-host
+  // MLA stack (1.72 GB, H2D-bound, bare copy 30.0 ms): 40 chunks of <= 32 MiB
+  // took 34-35 ms per replay, 25 chunks 31.1 ms, 16 chunks 30.9 ms, 8 chunks
+  // 30.7 ms. With many more commands per replay than the hardware queues
+  // hold, the host blocks mid-enqueue while the copy stream runs dry.
+  int64_t piped_need = 0;
+  for (int32_t o : piped) piped_need += need_of(L->outs[o]);
+  constexpr int64_t kTargetChunks = 16;
   const int64_t chunk_target =
-      (int64_t)(opts.chunk_bytes ? opts.chunk_bytes : std::min<uint64_t>(32ull << 20, std::max<uint64_t>(watermark / 2, 1)));
+      opts.chunk_bytes ? (int64_t)opts.chunk_bytes
+                       : std::max<int64_t>(std::min<int64_t>(std::max<int64_t>(piped_need / kTargetChunks, 32ll << 20),
+                                                             (int64_t)(watermark / 2)),
+                                           1);
 
   for (int32_t o : piped) {
     const int64_t need = need_of(L->outs[o]);

@@ -55,9 +55,11 @@ struct wt_plan {
 
   hipStream_t s_h2d = nullptr, s_prep = nullptr, s_out = nullptr;
   std::vector<hipEvent_t> ev_h2d, ev_prep, ev_rel;
-  hipEvent_t ev_start = nullptr, ev_out_end = nullptr, ev_done = nullptr;
-  bool has_prev = false;
+  hipEvent_t ev_start = nullptr, ev_out_end = nullptr;
+  hipEvent_t ev_done[2] = {nullptr, nullptr};  // end of replays with even / odd sequence numbers
+  uint64_t replays = 0;                         // pipelined replays enqueued so far
 
+  std::vector<char> rel_waited;  // per chunk: some later chunk waits for its release
   std::atomic<bool> busy{false};
   mutable std::mutex err_mu;
   std::string last_error;
@@ -192,7 +194,7 @@ void destroy_resources(wt_plan *p) {
   for (auto *v : {&p->ev_h2d, &p->ev_prep, &p->ev_rel})
     for (hipEvent_t e : *v)
       if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : {p->ev_start, p->ev_out_end, p->ev_done})
+  for (hipEvent_t e : {p->ev_start, p->ev_out_end, p->ev_done[0], p->ev_done[1]})
     if (e) (void)hipEventDestroy(e);
   for (hipStream_t s : {p->s_h2d, p->s_prep, p->s_out})
     if (s) (void)hipStreamDestroy(s);
@@ -300,7 +302,8 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
     }
     HIP_OR(p, hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming));
     HIP_OR(p, hipEventCreateWithFlags(&p->ev_out_end, hipEventDisableTiming));
-    HIP_OR(p, hipEventCreateWithFlags(&p->ev_done, hipEventDisableTiming));
+    HIP_OR(p, hipEventCreateWithFlags(&p->ev_done[0], hipEventDisableTiming));
+    HIP_OR(p, hipEventCreateWithFlags(&p->ev_done[1], hipEventDisableTiming));
   }
   return WT_OK;
 }
@@ -315,14 +318,29 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
     return WT_OK;
   }
   const int unit_base = p->direct_batch >= 0 ? 1 : 0;
+  // a chunk's release is recorded only when a later chunk waits for it
+  std::vector<char> &waited = p->rel_waited;
+  if (waited.size() != L.chunks.size()) {
+    waited.assign(L.chunks.size(), 0);
+    for (const Chunk &C : L.chunks)
+      if (C.wait_for >= 0) waited[C.wait_for] = 1;
+  }
   const bool staged = L.dst_mode == WT_DST_STAGED;
   const hipMemcpyKind out_kind = p->dst_kind == WT_MEM_DEVICE ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
 
+  // Backpressure: at most two replays of this plan in flight. Before
+  // enqueueing replay r the host waits for replay r - 2 to finish; the
+  // runtime otherwise throttles deep queues of copies by blocking single
+  // hipMemcpyAsync calls for milliseconds, in lockstep with the GPU, which
+  // left the copy engine idle between chunks (measured: 34 ms per replay of
+  // the pinned-host MLA stack back to back, 31 ms from idle).
+  const uint64_t r = p->replays;
+  if (r >= 2) HIP_OR(p, hipEventSynchronize(p->ev_done[r & 1]));
   // Order after the caller's prior work and after this plan's previous replay.
   HIP_OR(p, hipEventRecord(p->ev_start, user));
   for (hipStream_t s : {p->s_h2d, p->s_prep, p->s_out}) {
     HIP_OR(p, hipStreamWaitEvent(s, p->ev_start, 0));
-    if (p->has_prev) HIP_OR(p, hipStreamWaitEvent(s, p->ev_done, 0));
+    if (r > 0) HIP_OR(p, hipStreamWaitEvent(s, p->ev_done[(r - 1) & 1], 0));
   }
   if (p->direct_batch >= 0) {
     HIP_OR(p, launch_batch(p->batches[p->direct_batch], p->s_prep));
@@ -352,18 +370,18 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
         HIP_OR(p, hipMemcpyAsync(p->dst + d.dst_off, p->staging + C.slot_off + d.stage_off, (size_t)d.bytes,
                                  out_kind, p->s_out));
       if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress + unit_base + c, p->s_out));
-      HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_out));
+      if (waited[c]) HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_out));
     } else {
       if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress + unit_base + c, p->s_prep));
-      HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_prep));
+      if (waited[c]) HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_prep));
     }
   }
   // join: everything done -> ev_done on s_prep -> the caller's stream
   HIP_OR(p, hipEventRecord(p->ev_out_end, p->s_out));
   HIP_OR(p, hipStreamWaitEvent(p->s_prep, p->ev_out_end, 0));
-  HIP_OR(p, hipEventRecord(p->ev_done, p->s_prep));
-  HIP_OR(p, hipStreamWaitEvent(user, p->ev_done, 0));
-  p->has_prev = true;
+  HIP_OR(p, hipEventRecord(p->ev_done[r & 1], p->s_prep));
+  HIP_OR(p, hipStreamWaitEvent(user, p->ev_done[r & 1], 0));
+  p->replays = r + 1;
   return WT_OK;
 }
 

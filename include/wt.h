@@ -106,7 +106,11 @@ typedef struct wt_plan_options {
    * Default 256 MiB. */
   uint64_t watermark_bytes;
   /* Target bytes of one pipeline chunk (outputs moved through the stages
-   * together, one kernel launch each). Default: min(32 MiB, watermark/2). */
+   * together, one kernel launch each). 0 (default): about 1/16 of the bytes
+   * that go through the pipeline, at least 32 MiB, at most watermark / 2.
+   * Smaller chunks let the first parts of the destination region complete
+   * sooner (see the completion counters); many more than a few dozen chunks
+   * per replay cost throughput. */
   uint64_t chunk_bytes;
   int32_t dst_write_mode; /* WT_DST_ZERO_COPY (default) or WT_DST_STAGED */
   int32_t device;         /* HIP device ordinal; -1 (default) = current device */
@@ -184,9 +188,12 @@ wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t
  * on `stream`. Pinned-host shards or WT_DST_STAGED run the three-stage
  * pipeline (host-to-device copy, prepare, destination copy) on the plan's own
  * streams, one in-order queue per stage, and join `stream` at the end.
- * Returns without waiting for the GPU. No validation or allocation happens
- * here. Returns WT_E_STATE if another wt_prepare on the same plan is running
- * in another thread, WT_E_HIP on a runtime error. */
+ * Returns without waiting for the GPU, except that a pipelined plan keeps at
+ * most two replays in flight: replay r first waits on the host for replay
+ * r - 2 to finish (deeper queues of copies make the runtime block single
+ * copy submissions and starve the copy engine). No validation or allocation
+ * happens here. Returns WT_E_STATE if another wt_prepare on the same plan is
+ * running in another thread, WT_E_HIP on a runtime error. */
 wt_status wt_prepare(wt_plan *plan, void *stream);
 
 /* Copies the plan's shape into *info. */

@@ -232,3 +232,19 @@ def test_progress_wait_on_the_host(wt):
     th.start()
     assert wt.wt_progress_wait(a + 8, 1, 10 * 10**9)
     th.join()
+
+
+def test_default_chunking_bounds_chunk_count(wt):
+    # about 16 chunks per replay by default, at most watermark / 2 bytes each;
+    # an explicit chunk size is honoured
+    wl = W.mla_many_small(materialize=False)
+    tab = fake_table(wt, wl)
+    i = wt.wt_plan_check(tab, wl.dst_bytes, wt.WT_MEM_DEVICE)
+    assert 12 <= i["n_chunks"] <= 24
+    o = wt.wt_plan_options_init()
+    o.chunk_bytes = 8 << 20
+    assert wt.wt_plan_check(tab, wl.dst_bytes, wt.WT_MEM_DEVICE, o)["n_chunks"] > 40
+    o = wt.wt_plan_options_init()
+    o.watermark_bytes = 1 << 30
+    ops = wt.wt_plan_schedule(tab, wl.dst_bytes, opts=o)
+    assert max(op["staging_bytes"] for op in ops if op["stage"] == 0) <= (1 << 29) + (1 << 20)
