@@ -56,6 +56,7 @@ struct wt_plan {
   hipStream_t s_h2d = nullptr, s_prep = nullptr, s_out = nullptr;
   std::vector<hipEvent_t> ev_h2d, ev_prep, ev_rel;
   hipEvent_t ev_start = nullptr, ev_out_end = nullptr;
+  hipEvent_t ev_last = nullptr;  // after the latest launch on the caller's stream (plans without a pipeline)
   hipEvent_t ev_done[2] = {nullptr, nullptr};  // end of replays with even / odd sequence numbers
   uint64_t replays = 0;                         // pipelined replays enqueued so far
 
@@ -188,13 +189,14 @@ size_t blob_bytes(const std::vector<T> &v) {
 }
 
 void destroy_resources(wt_plan *p) {
+  if (p->ev_last) (void)hipEventSynchronize(p->ev_last);  // the tables are in use until then
   if (p->s_prep) (void)hipStreamSynchronize(p->s_prep);
   if (p->s_out) (void)hipStreamSynchronize(p->s_out);
   if (p->s_h2d) (void)hipStreamSynchronize(p->s_h2d);
   for (auto *v : {&p->ev_h2d, &p->ev_prep, &p->ev_rel})
     for (hipEvent_t e : *v)
       if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : {p->ev_start, p->ev_out_end, p->ev_done[0], p->ev_done[1]})
+  for (hipEvent_t e : {p->ev_start, p->ev_out_end, p->ev_done[0], p->ev_done[1], p->ev_last})
     if (e) (void)hipEventDestroy(e);
   for (hipStream_t s : {p->s_h2d, p->s_prep, p->s_out})
     if (s) (void)hipStreamDestroy(s);
@@ -287,6 +289,7 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
   p->epoch = (uint64_t *)(p->tables + epoch_off);
   HIP_OR(p, hipMemcpy(p->tables, blob.data(), total, hipMemcpyHostToDevice));
 
+  if (!p->pipeline) HIP_OR(p, hipEventCreateWithFlags(&p->ev_last, hipEventDisableTiming));
   if (p->pipeline) {
     HIP_OR(p, hipStreamCreateWithFlags(&p->s_h2d, hipStreamNonBlocking));
     HIP_OR(p, hipStreamCreateWithFlags(&p->s_prep, hipStreamNonBlocking));
@@ -315,6 +318,7 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
   if (!p->pipeline) {
     HIP_OR(p, launch_batch(p->batches[p->direct_batch], user));
     if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress, user));
+    HIP_OR(p, hipEventRecord(p->ev_last, user));
     return WT_OK;
   }
   const int unit_base = p->direct_batch >= 0 ? 1 : 0;

@@ -199,9 +199,10 @@ wt_status wt_prepare(wt_plan *plan, void *stream);
 /* Copies the plan's shape into *info. */
 wt_status wt_plan_get_info(const wt_plan *plan, wt_plan_info *info);
 
-/* Waits for the plan's streams, then frees everything the plan owns (device
- * tables, staging, streams, events). Never frees shards or the destination
- * region. NULL is ignored. */
+/* Waits for the plan's work already enqueued (its own streams, and for a
+ * plan without a pipeline the latest launch on the caller's stream), then
+ * frees everything the plan owns (device tables, staging, streams, events).
+ * Never frees shards or the destination region. NULL is ignored. */
 void wt_plan_destroy(wt_plan *plan);
 
 /* Static text for a status code. */

@@ -122,6 +122,24 @@ def test_new_contents_same_plan():
         wt.wt_plan_destroy(h)
 
 
+@pytest.mark.parametrize("host", [False, True])
+def test_destroy_right_after_prepare(host):
+    # destroy waits for the plan's enqueued work (the launch on the caller's
+    # stream, or the pipeline streams) before freeing its tables and staging
+    from bf16_fp8_weight_amd import wt
+    if host:
+        wl = W.mla_many_small(device="cuda", layers=1, n_small=100, host=True)
+    else:
+        wl = W.custom([(4096, 2048), (2048, 4096)], n_shards=4, device="cuda")
+    dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    h = wt.wt_plan_create(wt.task_table(wl), dst.data_ptr(), wl.dst_bytes)
+    wt.wt_prepare(h, s.cuda_stream)
+    wt.wt_plan_destroy(h)
+    s.synchronize()
+    assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
+
+
 def test_dense_7b_full():
     wl = W.dense_7b(device="cuda")
     _parity(wl)
