@@ -53,7 +53,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the preparation path does not "
-              "shard across GPUs in this build.", file=sys.stderr)
+              "shard across GPUs; run it with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
