@@ -14,8 +14,9 @@
  * (section "RDMA WRITE: one-sided transfers"); the destination side gets no
  * notification.
  *
- * Numerics of an FP8 output (the page says only "quantize if needed"; this
- * is the reading the library implements): OCP FP8 E4M3 ("e4m3fn", max 448,
+ * Numerics of an FP8 output (the page lists quantization as a step but fixes
+ * no format or rounding; this is the reading the library implements): OCP
+ * FP8 E4M3 ("e4m3fn", max 448,
  * no infinity) with one fp32 scale per 128x128 tile of the fused tensor,
  * s = amax / 448 (s = 1 for an all-zero tile), each element
  * cast(fl32(x / s)) with IEEE-rounded fp32 division and round-to-nearest-even

@@ -248,3 +248,16 @@ def test_default_chunking_bounds_chunk_count(wt):
     o.watermark_bytes = 1 << 30
     ops = wt.wt_plan_schedule(tab, wl.dst_bytes, opts=o)
     assert max(op["staging_bytes"] for op in ops if op["stage"] == 0) <= (1 << 29) + (1 << 20)
+
+
+def test_plain_c_program_uses_the_abi(wt, tmp_path):
+    # the header compiles as C99 and a C program linked against libwt.so drives
+    # the host-only entry points without the Python binding
+    exe = tmp_path / "c_abi_check"
+    libdir = os.path.dirname(wt.LIB_PATH)
+    src = os.path.join(ROOT, "tests", "c_abi", "c_abi_check.c")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    src, "-o", str(exe), f"-L{libdir}", f"-l:{os.path.basename(wt.LIB_PATH)}",
+                    f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "c abi ok" in r.stdout, r.stdout + r.stderr
