@@ -49,3 +49,30 @@ def test_schedule_per_source_plans_compose(make, n_sources):
             wt.wt_plan_destroy(h)
     assert used >= 2
     assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
+
+
+def test_source_plans_concurrently_on_separate_streams():
+    # one plan per source, all replayed at once on their own streams into the
+    # shared region (disjoint ranges): the result equals the oracle's image
+    from bf16_fp8_weight_amd import wt
+
+    wl = W.kimi_k2_expert_share(device="cuda", experts=6)
+    params, dsts = W.metadata(wl)
+    n_src = 3
+    sch = wt.Schedule(params, dsts, align=256, n_sources=n_src)
+    dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    tabs = [sch.tasks(s) for s in range(n_src)]
+    plans = [wt.wt_plan_create(t, dst.data_ptr(), wl.dst_bytes, wt.WT_MEM_DEVICE) for t in tabs if t.n]
+    streams = [torch.cuda.Stream() for _ in plans]
+    torch.cuda.synchronize()
+    try:
+        for _ in range(3):
+            for h, s in zip(plans, streams):
+                wt.wt_prepare(h, s.cuda_stream)
+        for s in streams:
+            s.synchronize()
+    finally:
+        for h in plans:
+            wt.wt_plan_destroy(h)
+    assert len(plans) == n_src
+    assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
