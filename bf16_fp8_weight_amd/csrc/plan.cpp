@@ -410,7 +410,20 @@ void build_tables(const Layout &L, const std::vector<int32_t> &outputs, const Ba
         const bool full = full_rows && (J + 1) * kTile <= H.cols;
         const TileItem item{out_idx, (uint32_t)I, (uint32_t)J, seg_base + (uint32_t)s};
         if (!fast) {
-          t->general.push_back(item);
+          GenDesc gd{};
+          gd.q = d.q + (uint64_t)(I * kTile) * (uint64_t)H.cols + (uint64_t)(J * kTile);
+          gd.s = d.s + 4 * ((uint64_t)I * (uint64_t)H.tiles_c + (uint64_t)J);
+          gd.C = (uint32_t)H.cols;
+          gd.nr = (uint16_t)std::min<int64_t>(kTile, H.rows - I * kTile);
+          gd.w = (uint16_t)std::min<int64_t>(kTile, H.cols - J * kTile);
+          gd.tile_row = (uint32_t)I;
+          gd.tile_col = (uint32_t)J;
+          gd.seg = seg_base + (uint32_t)s;
+          if (one_seg) {
+            const DevSeg &g = t->segs[seg_base + s];
+            gd.src = g.src + 2 * ((uint64_t)(I * kTile - g.row0) * (uint64_t)H.cols + (uint64_t)(J * kTile));
+          }
+          t->general.push_back(gd);
         } else if (!(full && one_seg)) {
           t->edge.push_back(item);
         } else {

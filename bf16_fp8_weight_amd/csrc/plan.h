@@ -80,7 +80,8 @@ struct HostTables {
   std::vector<DevOut> outs;
   std::vector<DevSeg> segs;
   std::vector<RegDesc> fast;
-  std::vector<TileItem> edge, general;
+  std::vector<TileItem> edge;
+  std::vector<GenDesc> general;
   std::vector<CopyItem> copies;
 };
 

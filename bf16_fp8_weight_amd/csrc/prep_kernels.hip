@@ -369,26 +369,30 @@ struct GenRow {
   uint32_t nblk;  // 16-byte blocks in the image
 };
 
-__device__ __forceinline__ void general_tile(const LaunchTables &T, const TileItem it, uint32_t *red, GenRow *rows,
+__device__ __forceinline__ void general_tile(const LaunchTables &T, const GenDesc &gd, uint32_t *red, GenRow *rows,
                                              uint4 *img) {
-  const DevOut o = ld_table(T.outs, it.out);
   const uint32_t tid = threadIdx.x;
-  const int64_t C = o.cols;
-  const int64_t r0 = (int64_t)it.tile_row * kTile;
-  const uint32_t nr = (uint32_t)min((int64_t)kTile, o.rows - r0);
-  const int64_t c0 = (int64_t)it.tile_col * kTile;
-  const uint32_t w = (uint32_t)min((int64_t)kTile, C - c0);
+  const int64_t C = gd.C;
+  const uint32_t nr = gd.nr;
+  const uint32_t w = gd.w;
 
-  // 1a. row addresses (the window's segments walked with scalar loads)
+  // 1a. row addresses: resolved at plan time when the tile's rows come from
+  // one shard, else the window's segments are walked with scalar loads
   {
-    const int64_t r = r0 + min(tid, nr - 1);
     uint64_t a = 0;
-    uint32_t si = it.seg;
-    DevSeg g = ld_table(T.segs, si);
-    for (;;) {
-      if (r >= g.row0 && r < g.row_end) a = g.src + 2 * ((uint64_t)(r - g.row0) * (uint64_t)C + (uint64_t)c0);
-      if (g.row_end >= r0 + nr) break;
-      g = ld_table(T.segs, ++si);
+    if (gd.src) {
+      a = gd.src + 2ull * (uint64_t)min(tid, nr - 1) * (uint64_t)C;
+    } else {
+      const int64_t r0 = (int64_t)gd.tile_row * kTile;
+      const int64_t c0 = (int64_t)gd.tile_col * kTile;
+      const int64_t r = r0 + min(tid, nr - 1);
+      uint32_t si = gd.seg;
+      DevSeg g = ld_table(T.segs, si);
+      for (;;) {
+        if (r >= g.row0 && r < g.row_end) a = g.src + 2 * ((uint64_t)(r - g.row0) * (uint64_t)C + (uint64_t)c0);
+        if (g.row_end >= r0 + nr) break;
+        g = ld_table(T.segs, ++si);
+      }
     }
     if (tid < nr) {
       GenRow gr;
@@ -437,7 +441,7 @@ __device__ __forceinline__ void general_tile(const LaunchTables &T, const TileIt
   }
   const TileQ t = tile_quant(block_max<GT / 64>(m, red));
   // 3. quantize and store
-  const uint64_t q0 = o.q + (uint64_t)r0 * (uint64_t)C + (uint64_t)c0 + j;
+  const uint64_t q0 = gd.q + j;
   if (t.recip) {
 #pragma unroll
     for (int k = 0; k < kTile / 2; ++k) {
@@ -451,7 +455,7 @@ __device__ __forceinline__ void general_tile(const LaunchTables &T, const TileIt
       if (col_ok && r < nr) st_global<uint8_t>(q0 + (uint64_t)r * (uint64_t)C, (uint8_t)quant1<false>(x[k], t));
     }
   }
-  if (tid == 0) st_global<float>(o.s + 4 * ((uint64_t)it.tile_row * (uint64_t)o.tiles_c + it.tile_col), t.s);
+  if (tid == 0) st_global<float>(gd.s, t.s);
 }
 
 // ------------------------------------------------------------ kernels

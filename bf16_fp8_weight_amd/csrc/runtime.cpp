@@ -273,7 +273,7 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
     T.segs = (const DevSeg *)(uintptr_t)put(t.segs);
     T.fast_tiles = (const RegDesc *)(uintptr_t)put(t.fast);
     T.edge_tiles = (const TileItem *)(uintptr_t)put(t.edge);
-    T.general_tiles = (const TileItem *)(uintptr_t)put(t.general);
+    T.general_tiles = (const GenDesc *)(uintptr_t)put(t.general);
     T.copies = (const CopyItem *)(uintptr_t)put(t.copies);
     if (t.fast.size() > UINT32_MAX / 2 || t.edge.size() > UINT32_MAX / 2 || t.general.size() > UINT32_MAX / 2 ||
         t.copies.size() > UINT32_MAX / 2) {

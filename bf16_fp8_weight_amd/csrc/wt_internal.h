@@ -47,6 +47,21 @@ struct TileItem {
 };
 static_assert(sizeof(TileItem) == 16, "TileItem layout");
 
+// One tile of the general path, every address resolved at plan time.
+struct GenDesc {
+  uint64_t src;       // BF16 address of element (0, 0) when all rows come from one shard, else 0
+  uint64_t q;         // FP8 address of element (0, 0)
+  uint64_t s;         // address of the tile's scale
+  uint32_t C;         // row length in elements (BF16 and FP8 rows alike)
+  uint16_t nr;        // rows in the tile (<= 128)
+  uint16_t w;         // columns in the tile (<= 128)
+  uint32_t tile_row;  // for the segment walk when src == 0
+  uint32_t tile_col;
+  uint32_t seg;       // first segment that can hold the tile's rows
+  uint32_t pad;
+};
+static_assert(sizeof(GenDesc) == 48, "GenDesc layout");
+
 // One regular tile (full 128 x 128, rows from one shard, aligned output),
 // with every address resolved at plan time: one scalar load per tile.
 struct RegDesc {
@@ -90,7 +105,7 @@ struct LaunchTables {
   const DevSeg *segs;
   const RegDesc *fast_tiles;      // regular tiles of kOutFast outputs: full, rows from one shard
   const TileItem *edge_tiles;     // other tiles of kOutFast outputs: partial, or rows from several shards
-  const TileItem *general_tiles;  // tiles of the other outputs
+  const GenDesc *general_tiles;   // tiles of the other outputs
   const CopyItem *copies;
   uint32_t n_fast;
   uint32_t n_edge;
