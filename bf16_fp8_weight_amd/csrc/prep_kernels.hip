@@ -343,7 +343,7 @@ __device__ __forceinline__ void copy_item(const CopyItem ci, int lane) {
 
 // ------------------------------------------------------------ general tiles
 // Any cols and alignment (ragged shapes, odd row lengths, unaligned
-// destinations). 256 threads per tile, three phases:
+// destinations). WT_GEN_THREADS threads per tile, three phases:
 //  1. each row's BF16 segment (2 w bytes at a 2-byte-aligned address a_r) is
 //     copied into LDS with aligned 16-byte loads covering [a_r & ~15, ...):
 //     every loaded 16-byte block holds at least one byte of the row, so it
@@ -353,12 +353,19 @@ __device__ __forceinline__ void copy_item(const CopyItem ci, int lane) {
 //  3. quantize and store with byte stores, a wave writing 64 consecutive
 //     bytes of one row per instruction.
 // WT_GEN_PACE: 0 = a thread's block loads all in flight (measured fastest
-// here: 1.09 ms on the 512-tensor ragged set vs 1.21 ms paced at 2), 2 / 4 =
-// at most that many per wave.
+// with 256 threads: 1.09 ms on the 512-tensor ragged set vs 1.21 ms paced at
+// 2), 2 / 4 = at most that many per wave.
 #ifndef WT_GEN_PACE
 #define WT_GEN_PACE 0
 #endif
-constexpr int GT = 256;
+// Threads per general tile, measured on the 512-tensor ragged set (ms per
+// launch): 256 1.054, 512 0.950, 1024 1.021.
+#ifndef WT_GEN_THREADS
+#define WT_GEN_THREADS 512
+#endif
+constexpr int GT = WT_GEN_THREADS;         // threads per general tile
+constexpr int GR = GT / 128;               // row groups: thread t owns column t % 128 of rows t / 128 + GR k
+static_assert(GT == 256 || GT == 512 || GT == 1024, "general tile block size");
 constexpr int GCH = 17;                    // 16-byte blocks that can cover a 256-byte row segment
 constexpr int GROW = GCH * 16;             // LDS bytes per row image
 constexpr int GPAIRS = (kTile * GCH + GT - 1) / GT;  // (row, block) pairs per thread
@@ -425,16 +432,16 @@ __device__ __forceinline__ void general_tile(const LaunchTables &T, const GenDes
       if (ok[k]) img[tid + GT * k] = v[k];
   }
   __syncthreads();
-  // 2. amax: thread t owns column t & 127 of rows (t >> 7) + 2 k
+  // 2. amax: thread t owns column t & 127 of rows (t >> 7) + GR k
   const uint32_t j = tid & 127;
   const uint32_t rb = tid >> 7;
   const bool col_ok = j < w;
-  uint32_t x[kTile / 2];
+  uint32_t x[kTile / GR];
   uint32_t m = 0;
   const uint8_t *bytes = reinterpret_cast<const uint8_t *>(img);
 #pragma unroll
-  for (int k = 0; k < kTile / 2; ++k) {
-    const uint32_t r = rb + 2 * k;
+  for (int k = 0; k < kTile / GR; ++k) {
+    const uint32_t r = rb + GR * k;
     x[k] = 0;
     if (col_ok && r < nr) x[k] = *reinterpret_cast<const uint16_t *>(bytes + r * GROW + rows[r].off + 2 * j);
     m = max(m, x[k] & 0x7FFFu);
@@ -444,14 +451,14 @@ __device__ __forceinline__ void general_tile(const LaunchTables &T, const GenDes
   const uint64_t q0 = gd.q + j;
   if (t.recip) {
 #pragma unroll
-    for (int k = 0; k < kTile / 2; ++k) {
-      const uint32_t r = rb + 2 * k;
+    for (int k = 0; k < kTile / GR; ++k) {
+      const uint32_t r = rb + GR * k;
       if (col_ok && r < nr) st_global<uint8_t>(q0 + (uint64_t)r * (uint64_t)C, (uint8_t)quant1<true>(x[k], t));
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kTile / 2; ++k) {
-      const uint32_t r = rb + 2 * k;
+    for (int k = 0; k < kTile / GR; ++k) {
+      const uint32_t r = rb + GR * k;
       if (col_ok && r < nr) st_global<uint8_t>(q0 + (uint64_t)r * (uint64_t)C, (uint8_t)quant1<false>(x[k], t));
     }
   }
