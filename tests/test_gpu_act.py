@@ -179,3 +179,40 @@ def test_argument_errors(wt):
     assert st(x=x.data_ptr() + 1) == wt.WT_E_ALIGN
     assert st(scales=sc.data_ptr() + 2) == wt.WT_E_ALIGN
     assert st(n_out=0, q=0, scales=0) == 0  # no-op
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_strides_and_gathers(wt, seed):
+    import random
+    rng = random.Random(seed)
+    cols = rng.choice([1, 5, 8, 64, 127, 128, 200, 1024, 1031, 7168])
+    n_rows = rng.randint(1, 300)
+    x_stride = cols + rng.choice([0, 0, 1, 8, 13])
+    nb = -(-cols // 128)
+    q_stride = cols + rng.choice([0, 0, 3, 8, 64])
+    s_stride = 4 * nb + rng.choice([0, 0, 4, 12])
+    if rng.random() < 0.5:
+        n_out = rng.randint(0, 400)
+        idx = torch.tensor([rng.randint(-3, n_rows + 2) for _ in range(n_out)], dtype=torch.int32, device="cuda")
+    else:
+        idx, n_out = None, rng.randint(0, n_rows + 3)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(900 + seed)
+    x_off = rng.choice([0, 0, 1])  # one element: breaks 16-byte alignment (general path)
+    base = W._activations((1, n_rows * x_stride + x_off), g, "cuda").reshape(-1)
+    host_out = rng.random() < 0.25
+    mk = (lambda n: torch.full((n,), 0xA5, dtype=torch.uint8).pin_memory()) if host_out else \
+        (lambda n: torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda"))
+    q = mk(max(1, n_out * q_stride))
+    sc = mk(max(1, n_out * s_stride))
+    s = torch.cuda.current_stream()
+    wt.wt_quantize_act_b128(base.data_ptr() + 2 * x_off, n_rows, cols, x_stride,
+                            idx.data_ptr() if idx is not None else 0, n_out, q.data_ptr(), q_stride,
+                            sc.data_ptr(), s_stride, s.cuda_stream)
+    s.synchronize()
+    x2d = base[x_off:].reshape(n_rows, x_stride)
+    wq, ws = _oracle(_u16(x2d), cols, idx, n_out, q_stride, s_stride)
+    gq = q.cpu().numpy()[: n_out * q_stride].reshape(n_out, q_stride)
+    gs = sc.cpu().numpy()[: n_out * s_stride].reshape(n_out, s_stride)
+    assert np.array_equal(gq, wq) and np.array_equal(gs, ws), \
+        f"seed {seed}: rows {n_rows} cols {cols} strides {x_stride}/{q_stride}/{s_stride} n_out {n_out}"
