@@ -39,8 +39,10 @@ __device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t *red) {
 // ------------------------------------------------------------ aligned tiles
 // Outputs with cols % 8 == 0 (and < 2^24), 16-byte aligned rows and 8-byte
 // aligned FP8 rows. A tile is 128 rows x 16 chunks of 8 columns (16 bytes of
-// BF16 each). A workgroup of TT threads takes one tile; thread t owns chunks
-// t + TT k (k < CH = 2048 / TT): row (t + TT k) / 16, chunk t % 16. Each
+// BF16 each). Full tiles whose rows come from one shard go two per workgroup
+// (group_tile below; a row band with an odd count ends with a single tile).
+// A workgroup of TT threads that takes one tile gives thread t the chunks
+// t + TT k (k < CH = 2048 / TT): row (t + TT k) / 16, chunk t % 16, so each
 // wave instruction reads four complete 256-byte tile rows and each FP8 store
 // writes four complete 128-byte rows.
 //

@@ -6,8 +6,8 @@ byte count (bench.py --calibrate-copy BYTES) with each counter. A counter's
 scale is the copy's known bytes over what the counter reports for it; the
 kernel's traffic per launch is its per-dispatch readings (KiB) times those
 scales. The result goes to profiles/traffic.json with the hash of the kernel
-sources it was measured with; bench.py reports it only while the hash still
-matches.
+sources it was measured with (their code, comments and layout left out);
+bench.py reports it only while the hash still matches.
 
     python -m bf16_fp8_weight_amd.traffic --kernel prep_fast_copy_kernel \\
         --workload kimi_k2_moe_96experts --copy-bytes 4228890624 \\
@@ -20,6 +20,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -28,11 +29,19 @@ ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = ("prep_kernels.hip", "fp8_math.h", "wt_internal.h")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that a
+    comment edit does not invalidate a measurement of unchanged code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_sha() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(PKG, "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
