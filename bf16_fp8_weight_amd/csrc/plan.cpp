@@ -348,12 +348,18 @@ wt_status build_layout(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, i
     HostTables t;
     build_tables(*L, L->direct, va, &t);
     I.n_launches += launches_for(t);
+    I.n_regular_items += (int64_t)t.fast.size();
+    I.n_edge_tiles += (int64_t)t.edge.size();
+    I.n_general_tiles += (int64_t)t.general.size();
   }
   for (const Chunk &C : L->chunks) {
     va.C = &C;
     HostTables t;
     build_tables(*L, C.outputs, va, &t);
     I.n_launches += launches_for(t);
+    I.n_regular_items += (int64_t)t.fast.size();
+    I.n_edge_tiles += (int64_t)t.edge.size();
+    I.n_general_tiles += (int64_t)t.general.size();
   }
   return WT_OK;
 }

@@ -66,8 +66,8 @@ class wt_plan_options(ctypes.Structure):
 class wt_plan_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "n_tasks", "n_outputs", "n_fp8_outputs", "n_copy_outputs", "n_tiles", "input_bytes", "output_bytes",
-        "n_launches", "n_chunks", "n_h2d_copies", "n_dst_copies", "staging_bytes", "n_units")] + [
-        ("reserved", ctypes.c_int64 * 3)]
+        "n_launches", "n_chunks", "n_h2d_copies", "n_dst_copies", "staging_bytes", "n_units", "n_regular_items",
+        "n_edge_tiles", "n_general_tiles")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_ if n != "reserved"}

@@ -140,7 +140,9 @@ typedef struct wt_plan_info {
   int64_t n_dst_copies;       /* staging-to-destination copies per wt_prepare */
   int64_t staging_bytes;      /* device staging allocated (<= watermark) */
   int64_t n_units;            /* completion units: the device-resident launch (if any), then each chunk */
-  int64_t reserved[3];
+  int64_t n_regular_items;    /* work items of full tiles on the aligned path (a pair of tiles is one item) */
+  int64_t n_edge_tiles;       /* aligned-path tiles that are partial or draw rows from several shards */
+  int64_t n_general_tiles;    /* tiles of outputs with ragged columns or unaligned addresses */
 } wt_plan_info;
 
 /* One operation of the replayed schedule, as listed by wt_plan_schedule. */

@@ -261,3 +261,21 @@ def test_plain_c_program_uses_the_abi(wt, tmp_path):
                     f"-Wl,-rpath,{libdir}"], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and "c abi ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_work_item_counts(wt):
+    # full single-shard tiles go in pairs on the aligned path; tiles across shards are edge tiles;
+    # ragged outputs go to the general path
+    wl = W.kimi_k2_expert_share(materialize=False)
+    i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
+    assert (i["n_regular_items"], i["n_edge_tiles"], i["n_general_tiles"]) == (wl.n_tiles // 2, 0, 0)
+    outs = [W.OutputSpec("t", W.FP8, 384, W._matrix_parts(["w"], [1536], 8))]  # 192-row shards, 3 tiles per band
+    wl = W.Workload("x", outs)
+    wl.dst_bytes = W.pack(outs)
+    i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
+    # 12 bands: 8 of them inside one shard (a pair + a single each), 4 straddle a shard boundary
+    assert (i["n_regular_items"], i["n_edge_tiles"], i["n_general_tiles"]) == (16, 12, 0)
+    wl = W.ragged_stress(materialize=False, n_tensors=16)
+    i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
+    assert i["n_general_tiles"] > 0
+    assert i["n_regular_items"] * 2 + i["n_edge_tiles"] + i["n_general_tiles"] >= i["n_tiles"]
