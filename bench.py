@@ -349,11 +349,35 @@ def _bench_act(args) -> int:
         ends[i].record(stream)
     torch.cuda.synchronize()
     bracketed = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps / 1e3
+    # the same launches replayed from a HIP graph (no host launch cost between them)
+    n_graph = 100
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        launch_on = lambda st: wt.wt_quantize_act_b128(wl.x.data_ptr(), wl.tokens, H, H, idx_ptr, n_out, q_ptr,
+                                                       wl.q_stride, s_ptr, wl.s_stride, st)
+        launch_on(side.cuda_stream)
+    side.synchronize()
+    with torch.cuda.graph(graph):
+        for _ in range(n_graph):
+            launch_on(torch.cuda.current_stream().cuda_stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(5):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_s = g0.elapsed_time(g1) / (5 * n_graph) / 1e3
+    del graph
     value = wl.input_bytes / avg_s / 1e9
     achieved = wl.algorithmic_bytes / avg_s / 1e9
     log(f"{wl.name}: {n_out} rows; back-to-back {avg_s * 1e6:.2f} us/launch, bracketed one by one "
-        f"{bracketed * 1e6:.2f} us; host wall {t_total / args.steps * 1e6:.2f} us/launch; "
-        f"HBM {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.3f}")
+        f"{bracketed * 1e6:.2f} us, from a graph {graph_s * 1e6:.2f} us; host wall {t_total / args.steps * 1e6:.2f} "
+        f"us/launch; HBM {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.3f} "
+        f"({wl.algorithmic_bytes / graph_s / 1e9 / HBM_PEAK_GBPS:.3f} from the graph)")
 
     cpu = None
     verified = None
@@ -400,6 +424,8 @@ def _bench_act(args) -> int:
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": wl.algorithmic_bytes, "avg_launch_ms": round(avg_s * 1e3, 6),
                      "launches_per_step": 1, "bracketed_launch_ms": round(bracketed * 1e3, 6),
+                     "graph_launch_ms": round(graph_s * 1e3, 6),
+                     "graph_frac": round(wl.algorithmic_bytes / graph_s / 1e9 / HBM_PEAK_GBPS, 4),
                      "host_wall_ms_per_launch": round(t_total / args.steps * 1e3, 6)},
         "cpu_baseline": cpu,
         "verified_vs_oracle": verified,
