@@ -314,6 +314,15 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
 wt_status prepare_impl(wt_plan *p, hipStream_t user) {
   const Layout &L = p->L;
   const bool progress = p->progress != nullptr;
+  if (p->pipeline) {
+    // a pipelined replay waits on the host (backpressure): not possible inside stream capture
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_OR(p, hipStreamIsCapturing(user, &cs));
+    if (cs != hipStreamCaptureStatusNone) {
+      set_err(p, "a pipelined plan cannot be replayed under stream capture");
+      return WT_E_STATE;
+    }
+  }
   if (progress) HIP_OR(p, launch_progress_begin(p->epoch, user));
   if (!p->pipeline) {
     HIP_OR(p, launch_batch(p->batches[p->direct_batch], user));

@@ -198,9 +198,9 @@ wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t
  * happens here. A plan without a pipeline may be replayed inside stream
  * capture (its launches, completion-word kernels and event record become
  * graph nodes; each graph replay is a replay of the plan); a pipelined plan
- * may not, since its backpressure waits on the host. Returns WT_E_STATE if
- * another wt_prepare on the same plan is running in another thread,
- * WT_E_HIP on a runtime error. */
+ * may not, since its backpressure waits on the host (WT_E_STATE, nothing
+ * enqueued). Returns WT_E_STATE if another wt_prepare on the same plan is
+ * running in another thread, WT_E_HIP on a runtime error. */
 wt_status wt_prepare(wt_plan *plan, void *stream);
 
 /* Copies the plan's shape into *info. */

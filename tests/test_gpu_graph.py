@@ -95,3 +95,20 @@ def test_captured_activation_quantization(wt):
         assert np.array_equal(q.cpu().numpy().reshape(1024, 7168), wq)
         assert np.array_equal(sc.cpu().numpy().reshape(1024, 224), ws)
     del graph
+
+
+def test_pipelined_plan_refuses_capture(wt):
+    wl = W.mla_many_small(device="cuda", layers=1, n_small=50, host=True)
+    dst = torch.zeros(wl.dst_bytes, dtype=torch.uint8, device="cuda")
+    plan = wt.Plan(wl, dst)
+    assert plan.info()["n_chunks"] > 0
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(wt.WtError) as e:
+        with torch.cuda.graph(graph):
+            plan.prepare(torch.cuda.current_stream().cuda_stream)
+    assert e.value.status == wt.WT_E_STATE
+    torch.cuda.synchronize()
+    plan.prepare(torch.cuda.current_stream().cuda_stream)  # still usable outside capture
+    torch.cuda.synchronize()
+    assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl, fill=0), wl)
+    plan.close()
