@@ -42,6 +42,7 @@ def main() -> int:
     ap.add_argument("--dst-kind", default="device", choices=["device", "pinned"],
                     help="destination region in device memory or pinned host memory")
     ap.add_argument("--watermark-mb", type=int, default=0, help="pipeline watermark (0 = library default)")
+    ap.add_argument("--chunk-mb", type=int, default=0, help="pipeline chunk target (0 = library default)")
     ap.add_argument("--load-hint", type=int, default=0, help="wt_plan_options.load_hint (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -84,6 +85,8 @@ def main() -> int:
     opts.dst_write_mode = wt.WT_DST_STAGED if args.dst_mode == "staged" else wt.WT_DST_ZERO_COPY
     if args.watermark_mb:
         opts.watermark_bytes = args.watermark_mb << 20
+    if args.chunk_mb:
+        opts.chunk_bytes = args.chunk_mb << 20
     opts.load_hint = args.load_hint
     plan = wt.Plan(wl, dst, dst_kind, opts)
     info = plan.info()

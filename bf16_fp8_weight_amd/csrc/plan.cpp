@@ -73,6 +73,8 @@ wt_status build_layout(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, i
   L->dst_mode = opts.dst_write_mode;
   if (opts.load_hint > WT_LOAD_STREAM) return fail(err, WT_E_INVAL, "load_hint out of range");
   L->load_hint = opts.load_hint;
+  if (opts.max_replays_in_flight > 8) return fail(err, WT_E_INVAL, "max_replays_in_flight above 8");
+  L->max_replays_in_flight = opts.max_replays_in_flight ? opts.max_replays_in_flight : 1;
 
   // ---- per-task checks, grouping into outputs (first appearance order)
   std::map<int32_t, int32_t> group_out;
@@ -178,19 +180,27 @@ wt_status build_layout(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, i
     if (staged) n += H.data_bytes + H.scale_bytes + 4 * (int64_t)kStageAlign;
     return (int64_t)align_up((uint64_t)n, kSlotAlign);
   };
-  // Default chunk size: about kTargetChunks chunks per replay, at least 32 MiB
-  // and at most half the watermark. Measured on MI355X with the pinned-host
-  // MLA stack (1.72 GB, H2D-bound, bare copy 30.0 ms): 40 chunks of <= 32 MiB
-  // took 34-35 ms per replay, 25 chunks 31.1 ms, 16 chunks 30.9 ms, 8 chunks
-  // 30.7 ms. With many more commands per replay than the hardware queues
-  // hold, the host blocks mid-enqueue while the copy stream runs dry.
+  // Default chunk size: about kTargetChunks chunks per replay, at least 32 MiB,
+  // and small enough that the ring holds one slot per stage that keeps a
+  // chunk's staging busy (host-to-device copy, prepare, destination copy):
+  // at most watermark / 2, or watermark / 3 when host-resident shards are
+  // staged in and outputs staged out. Measured on MI355X with the pinned-host
+  // MLA stack (1.72 GB, H2D-bound, bare copy 30.0 ms), one replay in flight:
+  // 17 chunks 30.8 ms per replay, 40 chunks 31.2 ms; staged into pinned host
+  // memory under a 256 MiB watermark, 24 chunks capped at watermark / 2 took
+  // 46.1 ms (two slots for three stages), 33 chunks of 64 MiB 33.7 ms.
   int64_t piped_need = 0;
-  for (int32_t o : piped) piped_need += need_of(L->outs[o]);
+  bool any_h2d = false;
+  for (int32_t o : piped) {
+    piped_need += need_of(L->outs[o]);
+    any_h2d |= L->outs[o].mem == WT_MEM_PINNED_HOST;
+  }
+  const int64_t busy_stages = (any_h2d && staged) ? 3 : 2;
   constexpr int64_t kTargetChunks = 16;
   const int64_t chunk_target =
       opts.chunk_bytes ? (int64_t)opts.chunk_bytes
                        : std::max<int64_t>(std::min<int64_t>(std::max<int64_t>(piped_need / kTargetChunks, 32ll << 20),
-                                                             (int64_t)(watermark / 2)),
+                                                             (int64_t)watermark / busy_stages),
                                            1);
 
   for (int32_t o : piped) {

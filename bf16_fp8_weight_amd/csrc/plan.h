@@ -67,6 +67,7 @@ struct Layout {
   int64_t staging_bytes = 0;
   int32_t dst_mode = WT_DST_ZERO_COPY;
   uint32_t load_hint = WT_LOAD_AUTO;
+  uint32_t max_replays_in_flight = 1;  // resolved host-side backpressure depth (pipelined plans)
   std::vector<int32_t> task_unit;  // completion unit of each task (direct launch, then chunks)
   wt_plan_info info{};
 };

@@ -57,8 +57,8 @@ struct wt_plan {
   std::vector<hipEvent_t> ev_h2d, ev_prep, ev_rel;
   hipEvent_t ev_start = nullptr, ev_out_end = nullptr;
   hipEvent_t ev_last = nullptr;  // after the latest launch on the caller's stream (plans without a pipeline)
-  hipEvent_t ev_done[2] = {nullptr, nullptr};  // end of replays with even / odd sequence numbers
-  uint64_t replays = 0;                         // pipelined replays enqueued so far
+  std::vector<hipEvent_t> ev_done;  // end of pipelined replay r at [r % size]: replays in flight
+  uint64_t replays = 0;             // pipelined replays enqueued so far
 
   std::vector<char> rel_waited;  // per chunk: some later chunk waits for its release
   std::atomic<bool> busy{false};
@@ -193,10 +193,10 @@ void destroy_resources(wt_plan *p) {
   if (p->s_prep) (void)hipStreamSynchronize(p->s_prep);
   if (p->s_out) (void)hipStreamSynchronize(p->s_out);
   if (p->s_h2d) (void)hipStreamSynchronize(p->s_h2d);
-  for (auto *v : {&p->ev_h2d, &p->ev_prep, &p->ev_rel})
+  for (auto *v : {&p->ev_h2d, &p->ev_prep, &p->ev_rel, &p->ev_done})
     for (hipEvent_t e : *v)
       if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : {p->ev_start, p->ev_out_end, p->ev_done[0], p->ev_done[1], p->ev_last})
+  for (hipEvent_t e : {p->ev_start, p->ev_out_end, p->ev_last})
     if (e) (void)hipEventDestroy(e);
   for (hipStream_t s : {p->s_h2d, p->s_prep, p->s_out})
     if (s) (void)hipStreamDestroy(s);
@@ -305,8 +305,8 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
     }
     HIP_OR(p, hipEventCreateWithFlags(&p->ev_start, hipEventDisableTiming));
     HIP_OR(p, hipEventCreateWithFlags(&p->ev_out_end, hipEventDisableTiming));
-    HIP_OR(p, hipEventCreateWithFlags(&p->ev_done[0], hipEventDisableTiming));
-    HIP_OR(p, hipEventCreateWithFlags(&p->ev_done[1], hipEventDisableTiming));
+    p->ev_done.assign(L.max_replays_in_flight, nullptr);
+    for (hipEvent_t &e : p->ev_done) HIP_OR(p, hipEventCreateWithFlags(&e, hipEventDisableTiming));
   }
   return WT_OK;
 }
@@ -341,19 +341,23 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
   const bool staged = L.dst_mode == WT_DST_STAGED;
   const hipMemcpyKind out_kind = p->dst_kind == WT_MEM_DEVICE ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
 
-  // Backpressure: at most two replays of this plan in flight. Before
-  // enqueueing replay r the host waits for replay r - 2 to finish; the
-  // runtime otherwise throttles deep queues of copies by blocking single
+  // Backpressure: before enqueueing replay r the host waits for replay
+  // r - D to finish (D = max_replays_in_flight, default 1). The runtime
+  // otherwise throttles deep queues of copies by blocking single
   // hipMemcpyAsync calls for milliseconds, in lockstep with the GPU, which
-  // left the copy engine idle between chunks (measured: 34 ms per replay of
-  // the pinned-host MLA stack back to back, 31 ms from idle).
+  // left the copy engine idle between chunks. Measured on MI355X with the
+  // pinned-host MLA stack: with D = 2, 17 chunks per replay ran back to back
+  // at the speed of a replay from idle but 33 chunks took 58 ms per replay
+  // instead of 33.5 (one call held for 121 ms); waiting for each chunk
+  // instead of each replay was slower still.
   const uint64_t r = p->replays;
-  if (r >= 2) HIP_OR(p, hipEventSynchronize(p->ev_done[r & 1]));
+  const size_t D = p->ev_done.size();
+  if (r >= D) HIP_OR(p, hipEventSynchronize(p->ev_done[r % D]));
   // Order after the caller's prior work and after this plan's previous replay.
   HIP_OR(p, hipEventRecord(p->ev_start, user));
   for (hipStream_t s : {p->s_h2d, p->s_prep, p->s_out}) {
     HIP_OR(p, hipStreamWaitEvent(s, p->ev_start, 0));
-    if (r > 0) HIP_OR(p, hipStreamWaitEvent(s, p->ev_done[(r - 1) & 1], 0));
+    if (r > 0) HIP_OR(p, hipStreamWaitEvent(s, p->ev_done[(r - 1) % D], 0));
   }
   if (p->direct_batch >= 0) {
     HIP_OR(p, launch_batch(p->batches[p->direct_batch], p->s_prep));
@@ -392,8 +396,8 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
   // join: everything done -> ev_done on s_prep -> the caller's stream
   HIP_OR(p, hipEventRecord(p->ev_out_end, p->s_out));
   HIP_OR(p, hipStreamWaitEvent(p->s_prep, p->ev_out_end, 0));
-  HIP_OR(p, hipEventRecord(p->ev_done[r & 1], p->s_prep));
-  HIP_OR(p, hipStreamWaitEvent(user, p->ev_done[r & 1], 0));
+  HIP_OR(p, hipEventRecord(p->ev_done[r % D], p->s_prep));
+  HIP_OR(p, hipStreamWaitEvent(user, p->ev_done[r % D], 0));
   p->replays = r + 1;
   return WT_OK;
 }
@@ -405,7 +409,7 @@ extern "C" {
 void wt_plan_options_init(wt_plan_options *opts) {
   if (!opts) return;
   std::memset(opts, 0, sizeof *opts);
-  opts->watermark_bytes = 256ull << 20;
+  opts->watermark_bytes = 512ull << 20;
   opts->chunk_bytes = 0;
   opts->dst_write_mode = WT_DST_ZERO_COPY;
   opts->device = -1;

@@ -59,7 +59,8 @@ class wt_plan_options(ctypes.Structure):
         ("dst_write_mode", ctypes.c_int32),
         ("device", ctypes.c_int32),
         ("load_hint", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32 * 5),
+        ("max_replays_in_flight", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32 * 4),
     ]
 
 

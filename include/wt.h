@@ -104,11 +104,15 @@ typedef struct wt_plan_options {
    * ("GPU memory usage control": a task starts only while in-flight
    * temporary memory is under a configurable watermark). Used for staging
    * of pinned-host shards and, in WT_DST_STAGED mode, of outputs.
-   * Default 256 MiB. */
+   * Default 512 MiB (a staged pipeline into pinned host memory with one
+   * 176 MB output per layer measured 39 ms per replay under 256 MiB, 34 ms
+   * under 512 MiB). */
   uint64_t watermark_bytes;
   /* Target bytes of one pipeline chunk (outputs moved through the stages
    * together, one kernel launch each). 0 (default): about 1/16 of the bytes
-   * that go through the pipeline, at least 32 MiB, at most watermark / 2.
+   * that go through the pipeline, at least 32 MiB, at most watermark / 2
+   * (watermark / 3 when both shards and outputs are staged, so that each of
+   * the three stages can hold a slot of the ring).
    * Smaller chunks let the first parts of the destination region complete
    * sooner (see the completion counters); many more than a few dozen chunks
    * per replay cost throughput. */
@@ -120,7 +124,13 @@ typedef struct wt_plan_options {
    * WT_LOAD_STREAM (non-temporal loads). Affects speed only, never results;
    * values above WT_LOAD_STREAM are WT_E_INVAL. */
   uint32_t load_hint;
-  uint32_t reserved[5];
+  /* Host-side backpressure of pipelined plans: wt_prepare first waits on the
+   * host until at most max_replays_in_flight - 1 earlier replays of the plan
+   * are unfinished. 0 (default): 1, i.e. a call returns once the previous
+   * replay has finished and this one is enqueued. Values above 8 are
+   * WT_E_INVAL. Affects speed and host blocking, never results. */
+  uint32_t max_replays_in_flight;
+  uint32_t reserved[4];
 } wt_plan_options;
 
 enum { WT_LOAD_AUTO = 0, WT_LOAD_PLAIN = 1, WT_LOAD_STREAM = 2 };
@@ -192,9 +202,10 @@ wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t
  * pipeline (host-to-device copy, prepare, destination copy) on the plan's own
  * streams, one in-order queue per stage, and join `stream` at the end.
  * Returns without waiting for the GPU, except that a pipelined plan keeps at
- * most two replays in flight: replay r first waits on the host for replay
- * r - 2 to finish (deeper queues of copies make the runtime block single
- * copy submissions and starve the copy engine). No validation or allocation
+ * most max_replays_in_flight replays enqueued and unfinished: by default a
+ * call first waits on the host for the plan's previous replay (deeper queues
+ * of copies make the runtime block single copy submissions in lockstep with
+ * the GPU and starve the copy engine). No validation or allocation
  * happens here. A plan without a pipeline may be replayed inside stream
  * capture (its launches, completion-word kernels and event record become
  * graph nodes; each graph replay is a replay of the plan); a pipelined plan

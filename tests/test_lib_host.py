@@ -45,7 +45,7 @@ def test_status_strings(wt):
 
 def test_options_defaults(wt):
     o = wt.wt_plan_options_init()
-    assert o.watermark_bytes == 256 << 20 and o.dst_write_mode == wt.WT_DST_ZERO_COPY and o.device == -1
+    assert o.watermark_bytes == 512 << 20 and o.dst_write_mode == wt.WT_DST_ZERO_COPY and o.device == -1
 
 
 def _one(wt, **kw):
@@ -101,6 +101,17 @@ def test_load_hint_range(wt):
         assert _status(wt, [_one(wt)], opts=o) == 0
     o.load_hint = 3
     assert _status(wt, [_one(wt)], opts=o) == wt.WT_E_INVAL
+
+
+def test_max_replays_in_flight_range(wt):
+    o = wt.wt_plan_options_init()
+    assert o.max_replays_in_flight == 0  # library default
+    for v in (1, 2, 8):
+        o.max_replays_in_flight = v
+        assert _status(wt, [_one(wt)], opts=o) == 0
+    o.max_replays_in_flight = 9
+    assert _status(wt, [_one(wt)], opts=o) == wt.WT_E_INVAL
+    assert "max_replays_in_flight" in wt.wt_plan_last_error(None)
 
 
 def test_fused_group_offsets_from_first_task(wt):
@@ -248,6 +259,29 @@ def test_default_chunking_bounds_chunk_count(wt):
     o.watermark_bytes = 1 << 30
     ops = wt.wt_plan_schedule(tab, wl.dst_bytes, opts=o)
     assert max(op["staging_bytes"] for op in ops if op["stage"] == 0) <= (1 << 29) + (1 << 20)
+
+
+def test_default_chunk_leaves_a_slot_per_busy_stage(wt):
+    # 64 host-resident 2048 x 4096 tensors (16 MiB each) under a 128 MiB
+    # watermark: when outputs are staged too, three stages hold staging at once
+    # and a default chunk takes at most a third of the watermark; with zero-copy
+    # outputs two stages do and the bound is half
+    rows, cols, n = 2048, 4096, 64
+    data, scales = rows * cols, (rows // 128) * (cols // 128) * 4
+    tasks = [{"shards": [(0x7F0000000000 + i * 2 * rows * cols, rows)], "shard_mem": wt.WT_MEM_PINNED_HOST,
+              "cols": cols, "dtype": wt.WT_FP8_E4M3FN_B128, "fusion_group": -1,
+              "dst_offset": i * data, "scale_offset": n * data + i * scales} for i in range(n)]
+    tab = wt.TaskTable(tasks)
+    wm = 128 << 20
+    slots = {}
+    for mode in (wt.WT_DST_STAGED, wt.WT_DST_ZERO_COPY):
+        o = wt.wt_plan_options_init()
+        o.watermark_bytes = wm
+        o.dst_write_mode = mode
+        ops = wt.wt_plan_schedule(tab, n * (data + scales), opts=o)
+        slots[mode] = max(op["staging_bytes"] for op in ops if op["stage"] == 0)
+    assert slots[wt.WT_DST_STAGED] <= wm // 3
+    assert wm // 3 < slots[wt.WT_DST_ZERO_COPY] <= wm // 2
 
 
 def test_plain_c_program_uses_the_abi(wt, tmp_path):
