@@ -21,7 +21,7 @@ int main(void) {
   /* options */
   wt_plan_options o;
   wt_plan_options_init(&o);
-  CHECK(o.watermark_bytes == 256ull << 20 && o.dst_write_mode == WT_DST_ZERO_COPY && o.device == -1);
+  CHECK(o.watermark_bytes == 512ull << 20 && o.dst_write_mode == WT_DST_ZERO_COPY && o.device == -1);
 
   /* one fused output [q; k] of 256 x 256 from two tasks with 2 shards each
      (made-up, aligned device addresses: nothing is dereferenced) */
