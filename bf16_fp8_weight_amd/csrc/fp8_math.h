@@ -143,6 +143,14 @@ __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const TileQ
   return r;
 }
 
+// Two packed BF16 -> two E4M3 bytes in bits 0-7 (low half) and 8-15 (high
+// half); bits 16-31 are left over from the input. Same arithmetic as quant4.
+template <bool Recip>
+__device__ __forceinline__ uint32_t quant2(uint32_t w, const TileQ &t) {
+  const float a = qdiv<Recip>(bf16_lo(w), t), b = qdiv<Recip>(bf16_hi(w), t);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), (int)w, false);
+}
+
 // One BF16 -> one E4M3 byte (same arithmetic as quant4, one lane).
 template <bool Recip>
 __device__ __forceinline__ uint32_t quant1(uint32_t xbits, const TileQ &t) {

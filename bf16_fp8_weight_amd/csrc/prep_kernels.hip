@@ -349,17 +349,13 @@ __device__ __forceinline__ void copy_item(const CopyItem ci, int lane) {
 //  1. each row's BF16 segment (2 w bytes at a 2-byte-aligned address a_r) is
 //     copied into LDS with aligned 16-byte loads covering [a_r & ~15, ...):
 //     every loaded 16-byte block holds at least one byte of the row, so it
-//     lies in a mapped page; the bytes outside the segment are never used;
+//     lies in a mapped page; the bytes outside the segment are never used.
+//     All of a thread's block loads are in flight at once (pacing them at 2
+//     or 4 per wave measured slower or equal);
 //  2. amax over the segment values read from LDS at any alignment; the
-//     values stay in registers;
-//  3. quantize and store with byte stores, a wave writing 64 consecutive
-//     bytes of one row per instruction.
-// WT_GEN_PACE: 0 = a thread's block loads all in flight (measured fastest
-// with 256 threads: 1.09 ms on the 512-tensor ragged set vs 1.21 ms paced at
-// 2), 2 / 4 = at most that many per wave.
-#ifndef WT_GEN_PACE
-#define WT_GEN_PACE 0
-#endif
+//     values stay in registers, two to a register;
+//  3. quantize two values per convert and store with byte stores, a wave
+//     writing 64 consecutive bytes of one row per instruction.
 // Threads per general tile, measured on the 512-tensor ragged set (ms per
 // launch): 256 1.054, 512 0.950, 1024 1.021.
 #ifndef WT_GEN_THREADS
@@ -378,23 +374,85 @@ struct GenRow {
   uint32_t nblk;  // 16-byte blocks in the image
 };
 
+// Step 3 of a general tile: x[k] holds rows rb + GR (2k) (low half) and
+// rb + GR (2k + 1) (high half) of the thread's column j. rb is the same for
+// all lanes of a wave, so the row address q (row rb) is wave-uniform and
+// advances with scalar adds; each lane adds its column.
+// Full tiles of rows shorter than 2^24 bytes: byte stores through a buffer
+// resource at the tile's first byte, the row offset in a scalar register and
+// the column in the vector offset, so addressing takes no vector ALU work
+// (all offsets stay below (kTile - 1) C + kTile < 2^31).
+template <bool Recip, int KP>
+__device__ __forceinline__ void general_store_full(const uint32_t (&x)[KP], const TileQ &t, uint64_t tile_q,
+                                                   uint32_t row_off, uint32_t step, uint32_t j) {
+  // raw buffer, no stride, no range limit (0x00020000: the word-3 value for
+  // gfx9-family raw byte buffers)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)tile_q, (short)0, (int)0xFFFFFFFF, 0x00020000);
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const uint32_t b = quant2<Recip>(x[k], t);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs, (int)j, (int)row_off, 0);
+    row_off += step;
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(b >> 8), rs, (int)j, (int)row_off, 0);
+    row_off += step;
+  }
+}
+
+template <bool Recip, bool Masked, int KP>
+__device__ __forceinline__ void general_store(const uint32_t (&x)[KP], const TileQ &t, uint64_t q, uint64_t step,
+                                              uint32_t j, uint32_t rb, uint32_t nr, bool col_ok) {
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const uint32_t r0 = rb + GR * 2 * k, r1 = r0 + GR;
+    const uint32_t b = quant2<Recip>(x[k], t);
+    if (!Masked || (col_ok && r0 < nr)) ((gptr<uint8_t>)(uintptr_t)q)[j] = (uint8_t)b;
+    q += step;
+    if (!Masked || (col_ok && r1 < nr)) ((gptr<uint8_t>)(uintptr_t)q)[j] = (uint8_t)(b >> 8);
+    q += step;
+  }
+}
+
 __device__ __forceinline__ void general_tile(const LaunchTables &T, const GenDesc &gd, uint32_t *red, GenRow *rows,
-                                             uint4 *img) {
+                                             uint32_t *rstart, uint4 *img) {
   const uint32_t tid = threadIdx.x;
   const int64_t C = gd.C;
   const uint32_t nr = gd.nr;
   const uint32_t w = gd.w;
+  constexpr int KR = kTile / GR;  // rows per thread in steps 2 and 3
 
-  // 1a. row addresses: resolved at plan time when the tile's rows come from
-  // one shard, else the window's segments are walked with scalar loads
-  {
-    uint64_t a = 0;
-    if (gd.src) {
-      a = gd.src + 2ull * (uint64_t)min(tid, nr - 1) * (uint64_t)C;
-    } else {
+  if (gd.src) {
+    // 1. rows from one shard: every row address is gd.src + 2 C r, so the
+    // block addresses and the LDS row starts are computed, not looked up
+    if (tid < kTile) {
+      const uint32_t off = (uint32_t)(gd.src + 2ull * tid * (uint64_t)C) & 15u;
+      // LDS byte offset of the row's first element, stored so that the KR
+      // rows a thread reads in step 2 (rows t / 128 + GR k) are consecutive
+      rstart[(tid % GR) * KR + tid / GR] = tid * GROW + off;
+    }
+    uint4 v[GPAIRS];
+    bool ok[GPAIRS];
+#pragma unroll
+    for (int k = 0; k < GPAIRS; ++k) {
+      const uint32_t p = tid + GT * k;
+      const uint32_t row = p / GCH, blk = p - row * GCH;
+      const uint64_t a = gd.src + 2ull * row * (uint64_t)C;
+      const uint32_t nblk = ((uint32_t)(a & 15) + 2 * w + 15) >> 4;
+      ok[k] = row < nr && blk < nblk;
+      v[k] = make_uint4(0, 0, 0, 0);
+      if (ok[k]) v[k] = ld_global<uint4>((a & ~(uint64_t)15) + 16ull * blk);
+    }
+#pragma unroll
+    for (int k = 0; k < GPAIRS; ++k)
+      if (ok[k]) img[tid + GT * k] = v[k];
+  } else {
+    // 1a. rows from several shards: each row's address is found by walking
+    // the window's segments with scalar loads and kept in an LDS row table
+    {
       const int64_t r0 = (int64_t)gd.tile_row * kTile;
       const int64_t c0 = (int64_t)gd.tile_col * kTile;
       const int64_t r = r0 + min(tid, nr - 1);
+      uint64_t a = 0;
       uint32_t si = gd.seg;
       DevSeg g = ld_table(T.segs, si);
       for (;;) {
@@ -402,67 +460,104 @@ __device__ __forceinline__ void general_tile(const LaunchTables &T, const GenDes
         if (g.row_end >= r0 + nr) break;
         g = ld_table(T.segs, ++si);
       }
+      if (tid < kTile) {
+        GenRow gr;
+        gr.base = a & ~(uint64_t)15;
+        gr.off = (uint32_t)(a & 15);
+        gr.nblk = (gr.off + 2 * w + 15) >> 4;
+        rows[tid] = gr;
+        rstart[(tid % GR) * KR + tid / GR] = tid * GROW + gr.off;
+      }
     }
-    if (tid < nr) {
-      GenRow gr;
-      gr.base = a & ~(uint64_t)15;
-      gr.off = (uint32_t)(a & 15);
-      gr.nblk = (gr.off + 2 * w + 15) >> 4;
-      rows[tid] = gr;
-    }
-  }
-  __syncthreads();
-  // 1b. aligned 16-byte blocks into the LDS row images
-  {
+    __syncthreads();
+    // 1b. aligned 16-byte blocks into the LDS row images; every LDS read of
+    // the row records is issued before the first global load
+    GenRow g[GPAIRS];
+#pragma unroll
+    for (int k = 0; k < GPAIRS; ++k) g[k] = rows[min((tid + GT * k) / GCH, (uint32_t)kTile - 1)];
     uint4 v[GPAIRS];
     bool ok[GPAIRS];
 #pragma unroll
     for (int k = 0; k < GPAIRS; ++k) {
       const uint32_t p = tid + GT * k;
       const uint32_t row = p / GCH, blk = p - row * GCH;
-      ok[k] = row < nr && blk < rows[min(row, (uint32_t)kTile - 1)].nblk;
+      ok[k] = row < nr && blk < g[k].nblk;
       v[k] = make_uint4(0, 0, 0, 0);
-      if (ok[k]) v[k] = ld_global<uint4>(rows[row].base + 16ull * blk);
-#if WT_GEN_PACE == 2
-      if (k & 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-#elif WT_GEN_PACE == 4
-      if ((k & 3) == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-#endif
+      if (ok[k]) v[k] = ld_global<uint4>(g[k].base + 16ull * blk);
     }
 #pragma unroll
     for (int k = 0; k < GPAIRS; ++k)
       if (ok[k]) img[tid + GT * k] = v[k];
   }
   __syncthreads();
-  // 2. amax: thread t owns column t & 127 of rows (t >> 7) + GR k
+  // 2. amax: thread t owns column t & 127 of rows (t >> 7) + GR k; the values
+  // are held two to a register (rows of k = 2i and 2i + 1). Every LDS read is
+  // unconditional (rows past the tile read stale bytes of their own image
+  // slot) and masked afterwards, so the reads issue back to back; full tiles
+  // (uniform branch) need no masks.
   const uint32_t j = tid & 127;
-  const uint32_t rb = tid >> 7;
+  const uint32_t rb = __builtin_amdgcn_readfirstlane(tid >> 7);  // the same for all lanes of a wave
+  const bool full = nr == kTile && w == kTile;
   const bool col_ok = j < w;
-  uint32_t x[kTile / GR];
+  constexpr int KP = KR / 2;
+  uint32_t x[KP];
   uint32_t m = 0;
   const uint8_t *bytes = reinterpret_cast<const uint8_t *>(img);
+  const uint4 *rs = reinterpret_cast<const uint4 *>(rstart + rb * KR);
+  if (full) {
 #pragma unroll
-  for (int k = 0; k < kTile / GR; ++k) {
-    const uint32_t r = rb + GR * k;
-    x[k] = 0;
-    if (col_ok && r < nr) x[k] = *reinterpret_cast<const uint16_t *>(bytes + r * GROW + rows[r].off + 2 * j);
-    m = max(m, x[k] & 0x7FFFu);
-  }
-  const TileQ t = tile_quant(block_max<GT / 64>(m, red));
-  // 3. quantize and store
-  const uint64_t q0 = gd.q + j;
-  if (t.recip) {
+    for (int i = 0; i < KR / 4; ++i) {
+      const uint4 o = rs[i];
+      const uint32_t offs[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-    for (int k = 0; k < kTile / GR; ++k) {
-      const uint32_t r = rb + GR * k;
-      if (col_ok && r < nr) st_global<uint8_t>(q0 + (uint64_t)r * (uint64_t)C, (uint8_t)quant1<true>(x[k], t));
+      for (int h = 0; h < 2; ++h) {
+        const int k = 2 * i + h;
+        const uint32_t lo = *reinterpret_cast<const uint16_t *>(bytes + offs[2 * h] + 2 * j);
+        const uint32_t hi = *reinterpret_cast<const uint16_t *>(bytes + offs[2 * h + 1] + 2 * j);
+        x[k] = lo | (hi << 16);
+        m = pk_max_u16(m, abs2(x[k]));
+      }
     }
   } else {
+    const uint32_t col_mask = 0u - (uint32_t)col_ok;
 #pragma unroll
-    for (int k = 0; k < kTile / GR; ++k) {
-      const uint32_t r = rb + GR * k;
-      if (col_ok && r < nr) st_global<uint8_t>(q0 + (uint64_t)r * (uint64_t)C, (uint8_t)quant1<false>(x[k], t));
+    for (int i = 0; i < KR / 4; ++i) {
+      const uint4 o = rs[i];
+      const uint32_t offs[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = 2 * i + h;
+        const uint32_t r0 = rb + GR * 2 * k, r1 = r0 + GR;
+        const uint32_t lo = *reinterpret_cast<const uint16_t *>(bytes + offs[2 * h] + 2 * j);
+        const uint32_t hi = *reinterpret_cast<const uint16_t *>(bytes + offs[2 * h + 1] + 2 * j);
+        const uint32_t keep = (0u - (uint32_t)(r0 < nr) & 0xFFFFu) | (0u - (uint32_t)(r1 < nr) & 0xFFFF0000u);
+        x[k] = (lo | (hi << 16)) & keep & col_mask;
+        m = pk_max_u16(m, abs2(x[k]));
+      }
     }
+  }
+  m = max(m & 0xFFFFu, m >> 16);
+  const TileQ t = tile_quant(block_max<GT / 64>(m, red));
+  // 3. quantize two held values per convert and store their bytes; the row
+  // pointer advances by GR rows per store
+  const uint32_t rbu = rb;
+  const uint64_t q = gd.q + (uint64_t)rbu * (uint64_t)C;
+  const uint64_t step = (uint64_t)GR * (uint64_t)C;
+  if (full && C < (1 << 24)) {
+    if (t.recip)
+      general_store_full<true>(x, t, gd.q, rbu * (uint32_t)C, GR * (uint32_t)C, j);
+    else
+      general_store_full<false>(x, t, gd.q, rbu * (uint32_t)C, GR * (uint32_t)C, j);
+  } else if (full) {
+    if (t.recip)
+      general_store<true, false>(x, t, q, step, j, rbu, nr, col_ok);
+    else
+      general_store<false, false>(x, t, q, step, j, rbu, nr, col_ok);
+  } else {
+    if (t.recip)
+      general_store<true, true>(x, t, q, step, j, rbu, nr, col_ok);
+    else
+      general_store<false, true>(x, t, q, step, j, rbu, nr, col_ok);
   }
   if (tid == 0) st_global<float>(gd.s, t.s);
 }
@@ -495,11 +590,25 @@ __global__ __launch_bounds__(TT) void prep_fast_copy_kernel(LaunchTables T) {
   if (ci < T.n_copies) copy_item(ld_table(T.copies, ci), threadIdx.x & 63);
 }
 
+// Workgroup b of a launch goes to XCD b % 8 (round-robin dispatch), and each
+// XCD has its own L2. A general tile's rows start at any 2-byte alignment, so
+// the first and last 128-byte line of each row segment are shared with the
+// tiles to its left and right, which follow it in the table. Giving XCD x the
+// contiguous range of tiles [x n / 8, (x + 1) n / 8), in order, lets those
+// neighbours fetch the shared lines from one L2 at about the same time instead
+// of from memory twice. A bijection on [0, n) for every n.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
+  constexpr uint32_t kXcds = 8;
+  const uint32_t per = n / kXcds, rem = n % kXcds, x = b % kXcds;
+  return x * per + min(x, rem) + b / kXcds;
+}
+
 __global__ __launch_bounds__(GT) void prep_general_kernel(LaunchTables T) {
   __shared__ uint32_t red[GT / 64];
   __shared__ GenRow rows[kTile];
+  __shared__ __align__(16) uint32_t rstart[kTile];
   __shared__ uint4 img[kTile * GCH];
-  general_tile(T, ld_table(T.general_tiles, blockIdx.x), red, rows, img);
+  general_tile(T, ld_table(T.general_tiles, xcd_contiguous(blockIdx.x, T.n_general)), red, rows, rstart, img);
 }
 
 // Element-function check: out[i * 65536 + x] for every BF16 x, four per
