@@ -85,6 +85,38 @@ def test_repeated_replays_on_one_stream(wt):
     assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
 
 
+@pytest.mark.parametrize("depth", [1, 2, 3])
+def test_replays_in_flight_keep_order(wt, depth):
+    # a staged plan over device-resident shards (pipelined), replayed back to
+    # back with max_replays_in_flight = depth; before each replay after the
+    # first a stream-ordered kernel negates every shard, so replay r reads
+    # (-1)^r x. Six negations bring the inputs back to x, which the last replay
+    # read: the final image is the oracle's unless replays overlap or reorder
+    wl = W.custom([(300, 512), (129, 17), (1000, 1024), (64, 64), (200, 300), (77, 129), (500, 256), (33, 1000)],
+                  n_shards=3, device="cuda")
+    o = wt.wt_plan_options_init()
+    o.dst_write_mode = wt.WT_DST_STAGED
+    o.watermark_bytes = 3 << 20  # the ring wraps, so slots are reused within and across replays
+    o.chunk_bytes = 128 << 10
+    o.max_replays_in_flight = depth
+    dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    h = wt.wt_plan_create(wt.task_table(wl), dst.data_ptr(), wl.dst_bytes, wt.WT_MEM_DEVICE, o)
+    try:
+        assert wt.wt_plan_get_info(h)["n_chunks"] > 2
+        s = torch.cuda.current_stream()
+        for r in range(7):
+            if r:
+                for out in wl.outputs:
+                    for part in out.parts:
+                        for sh in part.shards:
+                            sh.neg_()
+            wt.wt_prepare(h, s.cuda_stream)
+        s.synchronize()
+    finally:
+        wt.wt_plan_destroy(h)
+    assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
+
+
 def test_create_rejects_bad_memory(wt):
     wl = W.custom([(128, 128)], n_shards=2, device="cuda")
     dst = torch.zeros(wl.dst_bytes, dtype=torch.uint8, device="cuda")
