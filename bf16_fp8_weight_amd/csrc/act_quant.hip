@@ -8,11 +8,11 @@
 // fuses the sender's shuffle of tokens into send-buffer slots with the
 // quantization; rows whose index is out of range are skipped.
 //
-// Mapping: one 16-lane DPP row per block, lane l owns channels
-// [128 b + 8 l, +8): one 16-byte load and one 8-byte store per lane, so a
-// wave reads four blocks (1 KB) and writes 512 bytes per instruction. The
-// block's amax is a butterfly max over the 16 lanes (quad_perm, row half
-// mirror, row mirror), which leaves it in every lane of the row.
+// Mapping, aligned rows: eight lanes per block, lane l owning the block's
+// 16-byte chunks l and l + 8, so each load and store instruction covers
+// consecutive bytes across a wave and a wave holds eight blocks; the block's
+// amax is a DPP max over its eight lanes. Unaligned rows: one 16-lane DPP row
+// per block, 2-byte loads and byte stores.
 #include <hip/hip_runtime.h>
 
 #include "fp8_math.h"
@@ -23,9 +23,6 @@ namespace {
 
 #ifndef WT_ACT_THREADS
 #define WT_ACT_THREADS 256
-#endif
-#ifndef WT_ACT_K
-#define WT_ACT_K 1
 #endif
 // Cache hints, measured on MI355X for 4096 x 7168 (us per launch, back to
 // back): plain 16.47, non-temporal stores 16.94, non-temporal loads 18.84,
@@ -62,14 +59,16 @@ __device__ __forceinline__ void act_store8(uint64_t a, uint2 q) {
   st_global<uint2>(a, q);
 }
 constexpr int kActThreads = WT_ACT_THREADS;
-constexpr int kActGroups = kActThreads / 16;  // 16-lane groups per workgroup
-constexpr int kActK = WT_ACT_K;               // blocks per group (loads in flight per lane)
+constexpr int kActGroups = kActThreads / 16;  // 16-lane groups per workgroup (unaligned path)
 
-__device__ __forceinline__ uint32_t row16_max(uint32_t m) {
+// Max over the L lanes of each aligned L-lane group (DPP within 16-lane rows;
+// lanes read from outside the group take no part), left in every lane.
+template <int L>
+__device__ __forceinline__ uint32_t lanes_max(uint32_t m) {
   m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x0B1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
   m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x04E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));  // row_mirror
+  if (L >= 8) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  if (L >= 16) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));  // row_mirror
   return m;
 }
 
@@ -98,54 +97,93 @@ __device__ __forceinline__ BlockAt locate(const ActArgs &a, uint32_t gblk, uint3
   return p;
 }
 
-// Fast: cols, x_stride, q_stride multiples of 8, x 16-byte and q 8-byte
-// aligned; each group takes K blocks, all K loads issued before any use.
-// General (K = 1): any shape and alignment (2-byte loads, byte stores).
-template <bool Fast, int K>
+// Unaligned path (any shape and alignment): one block per 16-lane group, lane
+// l owns channels [128 b + 8 l, +8), read with 2-byte loads and written with
+// byte stores.
 __global__ void __launch_bounds__(kActThreads) act_quant_kernel(ActArgs a) {
   const uint32_t l = threadIdx.x & 15;
-  const uint32_t base = blockIdx.x * (uint32_t)(kActGroups * K) + (threadIdx.x >> 4);
-  BlockAt p[K];
-  uint32_t w[K][4];
+  const BlockAt p = locate(a, blockIdx.x * (uint32_t)kActGroups + (threadIdx.x >> 4), l);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  const uint64_t xrow = a.x + 2ull * (uint64_t)p.src * (uint64_t)a.x_stride;
+  if (p.has) {
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    p[k] = locate(a, base + (uint32_t)(k * kActGroups), l);
-    w[k][0] = w[k][1] = w[k][2] = w[k][3] = 0u;
-    const uint64_t xrow = a.x + 2ull * (uint64_t)p[k].src * (uint64_t)a.x_stride;
-    if (Fast) {
-      if (p[k].has) {
-        const uint4 v = act_load16(xrow + 2ull * (uint64_t)p[k].c);
-        w[k][0] = v.x, w[k][1] = v.y, w[k][2] = v.z, w[k][3] = v.w;
-      }
-    } else if (p[k].has) {
+    for (int e = 0; e < 8; ++e)
+      if (p.c + e < a.cols)
+        w[e >> 1] |= (uint32_t)ld_global<uint16_t>(xrow + 2ull * (uint64_t)(p.c + e)) << (16 * (e & 1));
+  }
+  uint32_t m = pk_max_u16(pk_max_u16(abs2(w[0]), abs2(w[1])), pk_max_u16(abs2(w[2]), abs2(w[3])));
+  m = lanes_max<16>(max(m & 0xFFFFu, m >> 16));  // every lane of the row takes part
+  if (!p.has) return;
+  const TileQ t = block_quant(m);
+  const uint64_t qrow = a.q + (uint64_t)p.i * (uint64_t)a.q_stride;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (p[k].c + e < a.cols)
-          w[k][e >> 1] |= (uint32_t)ld_global<uint16_t>(xrow + 2ull * (uint64_t)(p[k].c + e)) << (16 * (e & 1));
+  for (int e = 0; e < 8; ++e)
+    if (p.c + e < a.cols) {
+      const uint32_t xb = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t q = t.recip ? quant1<true>(xb, t) : quant1<false>(xb, t);
+      st_global<uint8_t>(qrow + (uint64_t)(p.c + e), (uint8_t)q);
+    }
+  if (l == 0) st_global<float>(a.s + (uint64_t)p.i * (uint64_t)a.s_stride + 4ull * p.b, t.s);
+}
+
+// Lanes per block on the aligned path: each lane owns 128 / L channels
+// (128 / (8 L) 16-byte chunks), so the per-block work (locating the block,
+// its scale and reciprocal, the lane reduction) is paid once per 128 / L
+// elements of each lane instead of once per 8.
+// Measured on MI355X (us per launch back to back; 4096 tokens x 7168 /
+// 128-token top-8 dispatch): 16 lanes 17.3 / 5.7, 8 lanes 16.1 / 5.2,
+// 4 lanes 16.6 / 5.3.
+#ifndef WT_ACT_LANES
+#define WT_ACT_LANES 8
+#endif
+constexpr int kActLanes = WT_ACT_LANES;
+static_assert(kActLanes == 4 || kActLanes == 8 || kActLanes == 16, "lanes per block");
+
+// Aligned path (cols, x_stride, q_stride multiples of 8, x 16-byte and q
+// 8-byte aligned): L lanes per block, lane l owns the block's 16-byte chunks
+// l, l + L, l + 2 L, ..., so that each load and store instruction covers
+// consecutive bytes across the lanes of a wave.
+template <int L>
+__global__ void __launch_bounds__(kActThreads) act_quant_wide_kernel(ActArgs a) {
+  constexpr int E = 128 / L;  // channels per lane
+  constexpr int NC = E / 8;   // 16-byte chunks per lane
+  constexpr int G = kActThreads / L;
+  const uint32_t l = threadIdx.x & (L - 1);
+  const uint32_t gblk = blockIdx.x * (uint32_t)G + threadIdx.x / L;
+  uint32_t i = 0, b = 0;
+  int64_t src = -1;
+  if (gblk < a.n_blocks) {
+    i = gblk / a.nb;
+    b = gblk - i * a.nb;
+    src = a.index ? (int64_t)ld_global<int32_t>(a.index + 4ull * i) : (int64_t)i;
+  }
+  const bool row_ok = src >= 0 && src < a.n_rows;
+  const int64_t c0 = 128 * (int64_t)b + 8 * (int64_t)l;  // channel of the lane's first chunk
+  const uint64_t xrow = a.x + 2ull * (uint64_t)(row_ok ? src : 0) * (uint64_t)a.x_stride;
+  uint32_t w[NC][4];
+#pragma unroll
+  for (int ch = 0; ch < NC; ++ch) {
+    w[ch][0] = w[ch][1] = w[ch][2] = w[ch][3] = 0u;
+    if (row_ok && c0 + 8 * L * ch < a.cols) {
+      const uint4 v = act_load16(xrow + 2ull * (uint64_t)(c0 + 8 * L * ch));
+      w[ch][0] = v.x, w[ch][1] = v.y, w[ch][2] = v.z, w[ch][3] = v.w;
     }
   }
+  uint32_t m = 0;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    uint32_t m = pk_max_u16(pk_max_u16(abs2(w[k][0]), abs2(w[k][1])), pk_max_u16(abs2(w[k][2]), abs2(w[k][3])));
-    m = row16_max(max(m & 0xFFFFu, m >> 16));  // every lane of the row takes part
-    if (p[k].has) {
-      const TileQ t = block_quant(m);
-      const uint64_t qrow = a.q + (uint64_t)p[k].i * (uint64_t)a.q_stride;
-      if (Fast) {
-        const uint2 q = t.recip ? quant8<true>(w[k], t) : quant8<false>(w[k], t);
-        act_store8(qrow + (uint64_t)p[k].c, q);
-      } else {
+  for (int ch = 0; ch < NC; ++ch)
+    m = pk_max_u16(m, pk_max_u16(pk_max_u16(abs2(w[ch][0]), abs2(w[ch][1])), pk_max_u16(abs2(w[ch][2]), abs2(w[ch][3]))));
+  m = lanes_max<L>(max(m & 0xFFFFu, m >> 16));  // every lane of the group takes part
+  if (!row_ok) return;
+  const TileQ t = block_quant(m);
+  const uint64_t qrow = a.q + (uint64_t)i * (uint64_t)a.q_stride;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (p[k].c + e < a.cols) {
-            const uint32_t xb = (w[k][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const uint32_t q = t.recip ? quant1<true>(xb, t) : quant1<false>(xb, t);
-            st_global<uint8_t>(qrow + (uint64_t)(p[k].c + e), (uint8_t)q);
-          }
-      }
-      if (l == 0) st_global<float>(a.s + (uint64_t)p[k].i * (uint64_t)a.s_stride + 4ull * p[k].b, t.s);
+  for (int ch = 0; ch < NC; ++ch)
+    if (c0 + 8 * L * ch < a.cols) {
+      const uint2 q = t.recip ? quant8<true>(w[ch], t) : quant8<false>(w[ch], t);
+      act_store8(qrow + (uint64_t)(c0 + 8 * L * ch), q);
     }
-  }
+  if (l == 0) st_global<float>(a.s + (uint64_t)i * (uint64_t)a.s_stride + 4ull * b, t.s);
 }
 
 }  // namespace
@@ -153,11 +191,12 @@ __global__ void __launch_bounds__(kActThreads) act_quant_kernel(ActArgs a) {
 hipError_t launch_act_quant(const ActArgs &a, bool fast, hipStream_t stream) {
   if (a.n_blocks == 0) return hipSuccess;
   if (fast) {
-    const dim3 grid((a.n_blocks + kActGroups * kActK - 1) / (kActGroups * kActK));
-    hipLaunchKernelGGL((act_quant_kernel<true, kActK>), grid, dim3(kActThreads), 0, stream, a);
+    constexpr int G = kActThreads / kActLanes;
+    const dim3 grid((a.n_blocks + G - 1) / G);
+    hipLaunchKernelGGL((act_quant_wide_kernel<kActLanes>), grid, dim3(kActThreads), 0, stream, a);
   } else {
     const dim3 grid((a.n_blocks + kActGroups - 1) / kActGroups);
-    hipLaunchKernelGGL((act_quant_kernel<false, 1>), grid, dim3(kActThreads), 0, stream, a);
+    hipLaunchKernelGGL(act_quant_kernel, grid, dim3(kActThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
