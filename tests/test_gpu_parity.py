@@ -180,6 +180,32 @@ def test_row_wider_than_fast_path_limit():
     _parity(W.custom([(2, (1 << 24) + 8)], n_shards=2, device="cuda", seed=32))
 
 
+def test_general_full_tiles_at_the_offset_limit():
+    # 128 x (2^24 - 1): an odd row length, so the general path; its full tiles
+    # store through 32-bit offsets that reach 127 C + 127, just under 2^31.
+    # The whole output would keep the oracle busy for minutes, so tile columns
+    # are checked one by one: a tile depends on its own 128 x 128 values only,
+    # so a 128-column slice of the input, prepared alone, gives the same bytes.
+    import oracle
+
+    C = (1 << 24) - 1
+    wl = W.custom([(128, C)], n_shards=2, device="cuda", seed=34)
+    got, info = run_library(wl)
+    tiles_c = -(-C // 128)
+    assert info["n_general_tiles"] == tiles_c
+    o = wl.outputs[0]
+    x = torch.cat(list(o.parts[0].shards), dim=0)
+    data = got[o.dst_offset:o.dst_offset + 128 * C].reshape(128, C)
+    for J in (0, 1, tiles_c // 2, tiles_c - 2, tiles_c - 1):
+        c0 = 128 * J
+        w = min(128, C - c0)
+        bits = x[:, c0:c0 + w].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+        want = oracle.prepare([oracle.Output(oracle.FP8_TILE128, w, [[bits]], 0, 128 * w)], 128 * w + 4,
+                              np.zeros(128 * w + 4, dtype=np.uint8))
+        assert np.array_equal(data[:, c0:c0 + w], want[:128 * w].reshape(128, w)), f"tile column {J}"
+        assert bytes(got[o.scale_offset + 4 * J:o.scale_offset + 4 * J + 4]) == bytes(want[128 * w:]), f"scale {J}"
+
+
 def test_single_large_tensor():
     # one 2 GiB tensor (2^30 elements) in 8 shards
     _parity(W.custom([(65536, 16384)], n_shards=8, device="cuda", seed=33))
