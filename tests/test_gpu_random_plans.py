@@ -7,6 +7,7 @@ shards, a device or pinned-host destination, zero-copy or staged writes,
 small watermarks and chunks (ring reuse), destination alignments of 2, 16
 or 256 bytes, and both load hints. The whole destination region (canary
 fill included) is compared with the oracle's image."""
+import os
 import random
 
 import pytest
@@ -41,7 +42,16 @@ def _draw(seed):
     return wl, rng
 
 
-@pytest.mark.parametrize("seed", range(48))
+def _seeds():
+    # WT_RANDOM_PLAN_SEEDS=lo:hi runs seeds lo..hi-1 instead of the default 48
+    spec = os.environ.get("WT_RANDOM_PLAN_SEEDS", "")
+    if spec:
+        lo, hi = (int(v) for v in spec.split(":"))
+        return range(lo, hi)
+    return range(48)
+
+
+@pytest.mark.parametrize("seed", _seeds())
 def test_random_plan(seed):
     from bf16_fp8_weight_amd import wt
 
