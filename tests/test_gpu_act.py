@@ -4,6 +4,8 @@ the MoE dispatch sender shape (128 tokens x 7168, top-8 gather into
 interleaved send-buffer slots), a 4096-token batch, ragged shapes and
 strides, unaligned addresses (general path), out-of-range and repeated
 indices, every finite BF16 magnitude, pinned-host outputs. Marked gpu."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -181,7 +183,16 @@ def test_argument_errors(wt):
     assert st(n_out=0, q=0, scales=0) == 0  # no-op
 
 
-@pytest.mark.parametrize("seed", range(24))
+def _seeds():
+    # WT_RANDOM_ACT_SEEDS=lo:hi runs seeds lo..hi-1 instead of the default 24
+    spec = os.environ.get("WT_RANDOM_ACT_SEEDS", "")
+    if spec:
+        lo, hi = (int(v) for v in spec.split(":"))
+        return range(lo, hi)
+    return range(24)
+
+
+@pytest.mark.parametrize("seed", _seeds())
 def test_random_shapes_strides_and_gathers(wt, seed):
     import random
     rng = random.Random(seed)
