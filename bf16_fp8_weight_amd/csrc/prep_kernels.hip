@@ -11,6 +11,8 @@
 // input byte is read once and every output byte written once.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "fp8_math.h"
 #include "wt_internal.h"
 
@@ -665,29 +667,39 @@ __global__ __launch_bounds__(256) void cast_range_kernel(uint32_t first, uint64_
 // Dynamic-LDS request that admits at most WT_BLOCKS_PER_CU workgroups of
 // prep_fast_copy_kernel per compute unit of the current device (0 when the
 // device's per-block limit does not allow the cap).
-static uint32_t pacing_lds() {
-  int dev = 0, lds_cu = 0, lds_blk = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
-      hipDeviceGetAttribute(&lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds_cu <= 0) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  const uint32_t lds = (uint32_t)lds_cu / (WT_BLOCKS_PER_CU + 1) + 1;
-  const uint32_t static_lds = 4 * TW;
-  return lds + static_lds <= (uint32_t)lds_blk ? lds : 0;
-}
+// Launch parameters of prep_fast_copy_kernel that depend on the device, found
+// once per device: the dynamic-LDS request that admits at most
+// WT_BLOCKS_PER_CU workgroups per compute unit (0 if the device cannot be
+// asked), and the number of workgroups that run in one round (compute units x
+// WT_BLOCKS_PER_CU; 0 if unknown, which keeps every launch paced).
+struct FastLaunchParams {
+  uint32_t lds = 0, one_round = 0;
+};
 
-// Workgroups of prep_fast_copy_kernel that run in one round on the current
-// device (compute units x WT_BLOCKS_PER_CU); 0 if the device cannot be asked.
-static uint32_t one_round_blocks() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+static FastLaunchParams fast_launch_params() {
+  constexpr int kMaxDevices = 64;
+  static FastLaunchParams cache[kMaxDevices];
+  static std::once_flag once[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
-    return 0;
+    return FastLaunchParams{};
   }
-  return (uint32_t)cus * WT_BLOCKS_PER_CU;
+  std::call_once(once[dev], [dev] {
+    FastLaunchParams p;
+    int lds_cu = 0, lds_blk = 0, cus = 0;
+    if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&lds_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && lds_cu > 0) {
+      const uint32_t lds = (uint32_t)lds_cu / (WT_BLOCKS_PER_CU + 1) + 1;
+      const uint32_t static_lds = 4 * TW;
+      p.lds = lds + static_lds <= (uint32_t)lds_blk ? lds : 0;
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      p.one_round = (uint32_t)cus * WT_BLOCKS_PER_CU;
+    (void)hipGetLastError();
+    cache[dev] = p;
+  });
+  return cache[dev];
 }
 
 hipError_t launch_batch(const LaunchTables &T, hipStream_t stream) {
@@ -695,14 +707,13 @@ hipError_t launch_batch(const LaunchTables &T, hipStream_t stream) {
   const uint64_t blocks = (uint64_t)T.n_fast + T.n_edge + copy_blocks;
   if (blocks > 0) {
     if (blocks > UINT32_MAX / TT) return hipErrorInvalidValue;
-    static const uint32_t lds = pacing_lds();
-    static const uint32_t one_round = one_round_blocks();
+    const FastLaunchParams lp = fast_launch_params();
     // Measured on MI355X, one dense layer of hidden size 1024 (720 tiles,
     // one round of workgroups): 15.5 us per launch paced, 14.2 unpaced.
-    if (blocks <= one_round)
-      hipLaunchKernelGGL(prep_fast_copy_kernel<false>, dim3((uint32_t)blocks), dim3(TT), lds, stream, T);
+    if (blocks <= lp.one_round)
+      hipLaunchKernelGGL(prep_fast_copy_kernel<false>, dim3((uint32_t)blocks), dim3(TT), lp.lds, stream, T);
     else
-      hipLaunchKernelGGL(prep_fast_copy_kernel<true>, dim3((uint32_t)blocks), dim3(TT), lds, stream, T);
+      hipLaunchKernelGGL(prep_fast_copy_kernel<true>, dim3((uint32_t)blocks), dim3(TT), lp.lds, stream, T);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
