@@ -180,15 +180,16 @@ def test_row_wider_than_fast_path_limit():
     _parity(W.custom([(2, (1 << 24) + 8)], n_shards=2, device="cuda", seed=32))
 
 
-def test_general_full_tiles_at_the_offset_limit():
-    # 128 x (2^24 - 1): an odd row length, so the general path; its full tiles
-    # store through 32-bit offsets that reach 127 C + 127, just under 2^31.
-    # The whole output would keep the oracle busy for minutes, so tile columns
-    # are checked one by one: a tile depends on its own 128 x 128 values only,
-    # so a 128-column slice of the input, prepared alone, gives the same bytes.
+@pytest.mark.parametrize("C", [(1 << 24) - 1, (1 << 24) + 1])
+def test_general_full_tiles_at_the_offset_limit(C):
+    # 128 x C with C odd, so the general path. Below 2^24 its full tiles store
+    # through 32-bit offsets that reach 127 C + 127, just under 2^31; above,
+    # they take 64-bit addresses. The whole output would keep the oracle busy
+    # for minutes, so tile columns are checked one by one: a tile depends on
+    # its own 128 x 128 values only, so a 128-column slice of the input,
+    # prepared alone, gives the same bytes.
     import oracle
 
-    C = (1 << 24) - 1
     wl = W.custom([(128, C)], n_shards=2, device="cuda", seed=34)
     got, info = run_library(wl)
     tiles_c = -(-C // 128)
