@@ -174,6 +174,14 @@ def test_extreme_magnitudes():
     _parity(_scaled_workload(shapes, scales, seed=31))
 
 
+def test_extreme_magnitudes_general_path():
+    # the same magnitudes on odd row lengths: full and partial general tiles
+    # through the IEEE-division branch (s < 2^-100), BF16 subnormals included
+    shapes = [(256, 385), (128, 129), (300, 257), (130, 1001), (256, 127)]
+    scales = [1e-30, 1e-36, 3e-39, 1e34, 1e-25]
+    _parity(_scaled_workload(shapes, scales, seed=35))
+
+
 def test_row_wider_than_fast_path_limit():
     # 2^24 + 8 columns: beyond the aligned path's 32-bit tile offsets, so the
     # general path takes it
