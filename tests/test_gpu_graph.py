@@ -3,7 +3,7 @@ plan with completion words, and the activation quantization, captured into a
 HIP graph (through torch.cuda.graph) and replayed several times with eager
 work and synchronisations in between; every replay is checked against the
 oracle (new shard contents each time) and the completion word against the
-number of replays."""
+number of replays. Pipelined plans refuse capture (WT_E_STATE)."""
 import numpy as np
 import pytest
 import torch
@@ -97,6 +97,15 @@ def test_captured_activation_quantization(wt):
     del graph
 
 
+def _refill_host(wl, step):
+    g = torch.Generator().manual_seed(900 + step)
+    for o in wl.outputs:
+        for p in o.parts:
+            for s in p.shards:
+                if s.numel():
+                    s.copy_((torch.randn(s.shape, generator=g) * 0.02 * (step + 1)).to(torch.bfloat16))
+
+
 def test_pipelined_plan_refuses_capture(wt):
     wl = W.mla_many_small(device="cuda", layers=1, n_small=50, host=True)
     dst = torch.zeros(wl.dst_bytes, dtype=torch.uint8, device="cuda")
@@ -111,4 +120,52 @@ def test_pipelined_plan_refuses_capture(wt):
     plan.prepare(torch.cuda.current_stream().cuda_stream)  # still usable outside capture
     torch.cuda.synchronize()
     assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl, fill=0), wl)
+    plan.close()
+
+
+@pytest.mark.skip(reason="capture of pipelined replays is withdrawn: a build that captured them (stage streams "
+                         "forked from and joined to the caller's stream, no host-side waits) ended in a "
+                         "segmentation fault inside the runtime's end of capture on MI355X, cause not found; "
+                         "pipelined plans return WT_E_STATE under capture (test_pipelined_plan_refuses_capture)")
+@pytest.mark.parametrize("mode", ["h2d_device_dst", "staged_host_dst"])
+def test_captured_pipelined_plan(wt, mode):
+    # shards in pinned host memory: the pipeline (host-to-device copies, one
+    # launch per chunk, and in staged mode copies into a pinned-host region)
+    # captured into a graph; new host contents before each replay, every
+    # replay compared with the oracle, then an eager replay after the graph's
+    wl = W.mla_many_small(device="cuda", layers=1, n_small=50, host=True)
+    o = wt.wt_plan_options_init()
+    # just above the largest output's staging (o: 117 MB of BF16 in, 176 MB
+    # staged in and out), so the ring is reused within the replay
+    o.watermark_bytes = 128 << 20
+    o.chunk_bytes = 8 << 20
+    if mode == "staged_host_dst":
+        o.watermark_bytes = 192 << 20
+        o.dst_write_mode = wt.WT_DST_STAGED
+        dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8).pin_memory()
+        kind = wt.WT_MEM_PINNED_HOST
+    else:
+        dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+        kind = wt.WT_MEM_DEVICE
+    plan = wt.Plan(wl, dst, kind, o)
+    assert plan.info()["n_chunks"] > 2
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up outside capture
+        plan.prepare(side.cuda_stream)
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan.prepare(torch.cuda.current_stream().cuda_stream)
+    for step in range(3):
+        _refill_host(wl, step)                   # host work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
+    _refill_host(wl, 7)
+    plan.prepare(torch.cuda.current_stream().cuda_stream)  # eager replay after the graph ones
+    torch.cuda.synchronize()
+    assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
+    del graph
     plan.close()
