@@ -44,6 +44,7 @@ def main() -> int:
     ap.add_argument("--watermark-mb", type=int, default=0, help="pipeline watermark (0 = library default)")
     ap.add_argument("--chunk-mb", type=int, default=0, help="pipeline chunk target (0 = library default)")
     ap.add_argument("--load-hint", type=int, default=0, help="wt_plan_options.load_hint (0 = library default)")
+    ap.add_argument("--tile-group", type=int, default=0, help="wt_plan_options.tile_group (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the workload, time a plain device-to-device copy of BYTES (counter calibration)")
@@ -88,6 +89,7 @@ def main() -> int:
     if args.chunk_mb:
         opts.chunk_bytes = args.chunk_mb << 20
     opts.load_hint = args.load_hint
+    opts.tile_group = args.tile_group
     plan = wt.Plan(wl, dst, dst_kind, opts)
     info = plan.info()
     log(f"plan: {info}")

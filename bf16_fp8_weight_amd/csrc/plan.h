@@ -68,6 +68,7 @@ struct Layout {
   int32_t dst_mode = WT_DST_ZERO_COPY;
   uint32_t load_hint = WT_LOAD_AUTO;
   uint32_t max_replays_in_flight = 1;  // resolved host-side backpressure depth (pipelined plans)
+  uint32_t tile_group = WT_GROUP_AUTO;
   std::vector<int32_t> task_unit;  // completion unit of each task (direct launch, then chunks)
   wt_plan_info info{};
 };

@@ -25,6 +25,7 @@ WT_MEM_PINNED_HOST = 1
 WT_DST_ZERO_COPY = 0
 WT_DST_STAGED = 1
 WT_LOAD_AUTO, WT_LOAD_PLAIN, WT_LOAD_STREAM = range(3)
+WT_GROUP_AUTO, WT_GROUP_SINGLE, WT_GROUP_PAIR = range(3)
 
 EXPORTS = [
     "wt_plan_options_init", "wt_plan_check", "wt_plan_schedule", "wt_plan_create", "wt_prepare",
@@ -60,7 +61,8 @@ class wt_plan_options(ctypes.Structure):
         ("device", ctypes.c_int32),
         ("load_hint", ctypes.c_uint32),
         ("max_replays_in_flight", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32 * 4),
+        ("tile_group", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32 * 3),
     ]
 
 

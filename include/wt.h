@@ -130,8 +130,17 @@ typedef struct wt_plan_options {
    * replay has finished and this one is enqueued. Values above 8 are
    * WT_E_INVAL. Affects speed and host blocking, never results. */
   uint32_t max_replays_in_flight;
-  uint32_t reserved[4];
+  /* Grouping of full 128 x 128 tiles on the aligned path: WT_GROUP_AUTO
+   * (default: adjacent full tiles of a row band two to a workgroup, except in
+   * a launch of at most 768 full tiles, which fits in one round of
+   * workgroups and is latency-bound: one tile each), WT_GROUP_SINGLE or
+   * WT_GROUP_PAIR. Affects speed only, never results; values above
+   * WT_GROUP_PAIR are WT_E_INVAL. */
+  uint32_t tile_group;
+  uint32_t reserved[3];
 } wt_plan_options;
+
+enum { WT_GROUP_AUTO = 0, WT_GROUP_SINGLE = 1, WT_GROUP_PAIR = 2 };
 
 enum { WT_LOAD_AUTO = 0, WT_LOAD_PLAIN = 1, WT_LOAD_STREAM = 2 };
 

@@ -55,6 +55,7 @@ def test_tile_groups_with_leftovers(hint):
                   dist="t")
     o = wt.wt_plan_options_init()
     o.load_hint = hint
+    o.tile_group = wt.WT_GROUP_PAIR  # a small plan: pairs only when asked for
     _parity(wl, opts=o)
 
 

@@ -114,6 +114,25 @@ def test_max_replays_in_flight_range(wt):
     assert "max_replays_in_flight" in wt.wt_plan_last_error(None)
 
 
+def test_tile_group_option(wt):
+    o = wt.wt_plan_options_init()
+    assert o.tile_group == wt.WT_GROUP_AUTO
+    o.tile_group = 3
+    assert _status(wt, [_one(wt)], opts=o) == wt.WT_E_INVAL
+    assert "tile_group" in wt.wt_plan_last_error(None)
+    # 768 full tiles (one round of workgroups) or fewer: single tiles by default;
+    # more: pairs; either forced by the option
+    for bands, auto_items in ((24, 24 * 32), (25, 25 * 16)):
+        outs = [W.OutputSpec("t", W.FP8, 4096, W._matrix_parts(["w"], [128 * bands], 1))]
+        wl = W.Workload("x", outs)
+        wl.dst_bytes = W.pack(outs)
+        want = {wt.WT_GROUP_AUTO: auto_items, wt.WT_GROUP_SINGLE: bands * 32, wt.WT_GROUP_PAIR: bands * 16}
+        for g, n in want.items():
+            o = wt.wt_plan_options_init()
+            o.tile_group = g
+            assert wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes, opts=o)["n_regular_items"] == n, (bands, g)
+
+
 def test_fused_group_offsets_from_first_task(wt):
     # the second member's offsets are ignored, so they may be anything
     ok = [_one(wt, fusion_group=1, scale_offset=1024), _one(wt, fusion_group=1, dst_offset=10 ** 9, scale_offset=10 ** 9)]
@@ -306,9 +325,14 @@ def test_work_item_counts(wt):
     outs = [W.OutputSpec("t", W.FP8, 384, W._matrix_parts(["w"], [1536], 8))]  # 192-row shards, 3 tiles per band
     wl = W.Workload("x", outs)
     wl.dst_bytes = W.pack(outs)
-    i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
+    o = wt.wt_plan_options_init()
+    o.tile_group = wt.WT_GROUP_PAIR
+    i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes, opts=o)
     # 12 bands: 8 of them inside one shard (a pair + a single each), 4 straddle a shard boundary
     assert (i["n_regular_items"], i["n_edge_tiles"], i["n_general_tiles"]) == (16, 12, 0)
+    # 36 tiles fit in one round of workgroups: by default every full tile is its own item
+    i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
+    assert (i["n_regular_items"], i["n_edge_tiles"], i["n_general_tiles"]) == (24, 12, 0)
     wl = W.ragged_stress(materialize=False, n_tensors=16)
     i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
     assert i["n_general_tiles"] > 0
