@@ -74,3 +74,62 @@ def test_random_plan(seed):
         f"watermark {o.watermark_bytes >> 10} KiB, chunks {info['n_chunks']}, launches {info['n_launches']}")
     got, _ = run_library(wl, dst_kind=dst_kind, opts=o, table=tab)
     assert_images_equal(got, oracle_image_threaded(wl), wl)
+
+
+def _replay_seeds():
+    # WT_RANDOM_REPLAY_SEEDS=lo:hi runs seeds lo..hi-1 instead of the default 16
+    spec = os.environ.get("WT_RANDOM_REPLAY_SEEDS", "")
+    if spec:
+        lo, hi = (int(v) for v in spec.split(":"))
+        return range(lo, hi)
+    return range(10000, 10016)
+
+
+@pytest.mark.parametrize("seed", _replay_seeds())
+def test_random_plan_replays(seed):
+    # the same draws, replayed three times back to back with a random replay
+    # depth and tile grouping; before the second and third replay every shard
+    # is negated (device shards by a kernel on the replay stream, host shards
+    # by the host after a synchronisation), so two negations bring the inputs
+    # back to those the last replay read: the final image is the oracle's
+    from bf16_fp8_weight_amd import wt
+
+    wl, rng = _draw(seed)
+    dst_kind = wt.WT_MEM_PINNED_HOST if rng.random() < 0.3 else wt.WT_MEM_DEVICE
+    o = wt.wt_plan_options_init()
+    o.dst_write_mode = wt.WT_DST_STAGED if rng.random() < 0.3 else wt.WT_DST_ZERO_COPY
+    o.chunk_bytes = rng.choice([0, 64 << 10, 1 << 20])
+    o.max_replays_in_flight = rng.choice([0, 1, 2, 3])
+    o.tile_group = rng.choice([wt.WT_GROUP_AUTO, wt.WT_GROUP_SINGLE, wt.WT_GROUP_PAIR])
+    o.watermark_bytes = 256 << 10
+    tab = wt.task_table(wl)
+    while True:
+        try:
+            wt.wt_plan_check(tab, wl.dst_bytes, dst_kind, o)
+            break
+        except wt.WtError as e:
+            assert e.status == wt.WT_E_WATERMARK, str(e)
+            o.watermark_bytes *= 2
+    if dst_kind == wt.WT_MEM_DEVICE:
+        dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    else:
+        dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8).pin_memory()
+    h = wt.wt_plan_create(tab, dst.data_ptr(), wl.dst_bytes, dst_kind, o)
+    host = wl.shard_mem == "host"
+    try:
+        s = torch.cuda.current_stream()
+        for r in range(3):
+            if r:
+                if host:
+                    s.synchronize()
+                for out in wl.outputs:
+                    for part in out.parts:
+                        for sh in part.shards:
+                            sh.neg_()
+            wt.wt_prepare(h, s.cuda_stream)
+        s.synchronize()
+    finally:
+        wt.wt_plan_destroy(h)
+    log(f"  seed {seed}: {len(wl.outputs)} outputs, {wl.shard_mem} shards, depth {o.max_replays_in_flight}, "
+        f"group {o.tile_group}, mode {o.dst_write_mode}")
+    assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
