@@ -424,6 +424,12 @@ class Plan:
             wt_plan_destroy(self.handle)
             self.handle = 0
 
+    def __enter__(self) -> "Plan":
+        return self
+
+    def __exit__(self, *exc) -> None:
+        self.close()
+
     def __del__(self):
         try:
             self.close()

@@ -59,6 +59,19 @@ def test_tile_groups_with_leftovers(hint):
     _parity(wl, opts=o)
 
 
+def test_plan_context_manager():
+    # the binding's Plan destroys its plan when the with-block ends
+    from bf16_fp8_weight_amd import wt
+
+    wl = W.custom([(256, 384)], n_shards=2, device="cuda", seed=36)
+    dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    with wt.Plan(wl, dst) as plan:
+        plan.prepare(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    assert plan.handle == 0
+    assert_images_equal(dst.cpu().numpy(), oracle_image_threaded(wl), wl)
+
+
 def test_ragged_stress_reduced():
     wl = W.ragged_stress(device="cuda", n_tensors=40, max_dim=1400)
     _parity(wl)
