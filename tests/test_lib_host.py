@@ -4,6 +4,7 @@ behaves as documented. No GPU call is made here."""
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -337,3 +338,11 @@ def test_work_item_counts(wt):
     i = wt.wt_plan_check(fake_table(wt, wl), wl.dst_bytes)
     assert i["n_general_tiles"] > 0
     assert i["n_regular_items"] * 2 + i["n_edge_tiles"] + i["n_general_tiles"] >= i["n_tiles"]
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    # no fallback of any kind: importing the binding with the library missing raises
+    env = dict(os.environ, WT_LIB=str(tmp_path / "missing" / "libwt.so"))
+    r = subprocess.run([sys.executable, "-c", "import bf16_fp8_weight_amd.wt"], capture_output=True, text=True,
+                       timeout=120, cwd=ROOT, env=env)
+    assert r.returncode != 0 and "ImportError" in r.stderr
