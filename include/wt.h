@@ -100,10 +100,10 @@ typedef struct wt_task {
 
 /* Plan options; wt_plan_options_init() fills the defaults. */
 typedef struct wt_plan_options {
-  /* Upper bound on temporary device memory held by tasks in flight
-   * ("GPU memory usage control": a task starts only while in-flight
-   * temporary memory is under a configurable watermark). Used for staging
-   * of pinned-host shards and, in WT_DST_STAGED mode, of outputs.
+  /* Upper bound on temporary device memory held by tasks in flight (the
+   * watermark of the weight-transfer page's section "GPU memory usage
+   * control", under which tasks are admitted). Used for staging of
+   * pinned-host shards and, in WT_DST_STAGED mode, of outputs.
    * Default 512 MiB (a staged pipeline into pinned host memory with one
    * 176 MB output per layer measured 39 ms per replay under 256 MiB, 34 ms
    * under 512 MiB). */
