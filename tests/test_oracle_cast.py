@@ -82,3 +82,48 @@ def test_cast_all_fp32_patterns_vs_midpoint_table(oracle_lib):
         x = (np.arange(step, dtype=np.uint64) + first).astype(np.uint32).view(np.float32)
         want = brute.midpoint_table_cast(x)
         assert np.array_equal(got, want), hex(first)
+
+
+def _range_bits(first, count):
+    return ((np.arange(count, dtype=np.uint64) + np.uint64(first)) & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+
+
+def _range_windows():
+    """(first, count) windows of consecutive fp32 patterns: zero and the
+    subnormals above it, every E4M3 rounding boundary (the midpoints between
+    adjacent E4M3 magnitudes) of both signs with its fp32 neighbours, the
+    saturation threshold 448 and the first non-representable magnitudes
+    above it, infinity and the NaNs past it (both signs), and a window that
+    wraps past 0xFFFFFFFF back to 0."""
+    w = [(0, 1 << 20), (0x80000000, 1 << 16), (0x3A000000, 1 << 22)]
+    mids = ((brute.VALS[1:] + brute.VALS[:-1]) / 2).astype(np.float32).view(np.uint32)
+    for m in mids:
+        w.append((int(m) - 32, 64))
+        w.append((int(m | 0x80000000) - 32, 64))
+    for centre in (0x43E00000, 0x43E80000, 0x43F00000, 0x7F800000, 0xFF800000):
+        w.append((centre - 4096, 8192))
+    w.append((0xFFFFF000, 0x2000))
+    return w
+
+
+def test_cast_f32_range_windows_vs_midpoint_table(oracle_lib):
+    # oracle_cast_f32_range walks consecutive fp32 patterns first + i
+    # (modulo 2^32); checked window by window against the test-side
+    # midpoint-table cast of the same patterns, and against brute-force
+    # nearest search on the boundary windows
+    for first, count in _range_windows():
+        got = oracle_lib.cast_f32_range(first, count)
+        x = _range_bits(first, count).view(np.float32)
+        want = brute.midpoint_table_cast(x)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (hex(first), [(hex(int(x.view(np.uint32)[i])), hex(got[i]), hex(want[i]))
+                                            for i in bad[:5]])
+        if count <= 8192:
+            assert np.array_equal(got, brute.nearest_even_bruteforce(x)), hex(first)
+
+
+def test_cast_f32_range_wraps_modulo_2_32(oracle_lib):
+    # the window crossing 0xFFFFFFFF ends with the largest-magnitude negative
+    # NaN patterns (-> 0xFF) and continues at +0 (-> 0x00)
+    got = oracle_lib.cast_f32_range(0xFFFFFFFE, 4)
+    assert list(got) == [0xFF, 0xFF, 0x00, 0x00]

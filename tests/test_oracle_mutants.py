@@ -43,6 +43,11 @@ MUTANTS = [
     ("components_overwrite", "fused_row += Rc;", "fused_row += 0;"),
     ("tile_rows_127", "const int64_t r0 = 128 * I, r1 = (128 * I + 128 < R) ? 128 * I + 128 : R;",
      "const int64_t r0 = 128 * I, r1 = (128 * I + 127 < R) ? 128 * I + 127 : R;"),
+    # fp32 pattern ranges (the reference of the exhaustive cast check)
+    ("range_offset_by_one", "const uint32_t bits = first + (uint32_t)i;",
+     "const uint32_t bits = first + (uint32_t)i + 1u;"),
+    ("range_saturates_instead_of_wrapping", "const uint32_t bits = first + (uint32_t)i;",
+     "const uint32_t bits = (uint64_t)first + i > 0xFFFFFFFFull ? 0xFFFFFFFFu : first + (uint32_t)i;"),
     # block-scaled activations
     ("act_block_127", "const int64_t c0 = 128 * b, c1 = (c0 + 128 < cols) ? c0 + 128 : cols;",
      "const int64_t c0 = 128 * b, c1 = (c0 + 127 < cols) ? c0 + 127 : cols;"),
