@@ -48,7 +48,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of the workload, time a plain device-to-device copy of BYTES (counter calibration)")
-    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0 = min(16, cores))")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads for the all-cores leg (0 = the CPU share: min(16, usable cores))")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="time only the chosen workload (default: after the Kimi-K2 share, also the dense 7B "
+                         "model, the ragged set and the pinned-host MLA pipeline, each verified)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters for the current kernel")
     args = ap.parse_args()
@@ -59,19 +63,74 @@ def main() -> int:
         return 2
 
     import torch
-    from bf16_fp8_weight_amd import workloads as W
-    from bf16_fp8_weight_amd import wt
+    from bf16_fp8_weight_amd import wt  # noqa: F401  (raises when the library is not built)
 
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         return _copy_calibration(args.calibrate_copy, args.steps, args.warmup)
     if args.workload.startswith("act_"):
         return _bench_act(args)
+    res = _bench_prepare(args.workload, args, traffic_json=args.traffic_json, progress=True)
+    res.pop("_wl")
+    cpu, verified = res.pop("cpu_baseline"), res.pop("verified_vs_oracle")
+    secondary = None
+    if not args.no_secondary and args.workload == "kimi_k2_moe":
+        secondary = {}
+        for name in ("dense_7b", "ragged_stress", "mla_many_small"):
+            r = _bench_prepare(name, args, baseline=False)
+            r.pop("_wl")
+            r.pop("cpu_baseline")
+            secondary[name] = r
+        if any(r["verified_vs_oracle"] is False for r in secondary.values()):
+            verified = False
+
+    line = {
+        "metric": "prepared BF16 GB/s (shard gather+fuse+FP8 quant+pack) and % of HBM peak",
+        "value": res["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: seeded N(0, 0.02) BF16, random weights of the stated shapes",
+        "config": res["config"],
+        "pct_hbm_peak": res["roofline"]["frac"],
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "verified_vs_oracle": verified,
+    }
+    if "pipeline" in res:
+        line["pipeline"] = res["pipeline"]
+    if secondary is not None:
+        line["secondary"] = secondary
+    print(json.dumps(line), flush=True)
+    return 0 if verified in (None, True) else 1
+
+
+def _shards_per_tensor(wl):
+    counts = sorted({len(p.shard_rows) for o in wl.outputs for p in o.parts})
+    return counts[0] if len(counts) == 1 else f"{counts[0]}-{counts[-1]}"
+
+
+def _bench_prepare(name: str, args, traffic_json: str | None = None, progress: bool = False,
+                   baseline: bool = True) -> dict:
+    """Builds workload `name` on the GPU, times args.steps replays of its plan
+    (HIP events on the launch stream around every replay, wall clock around
+    all of them), then compares the whole destination image with the oracle's
+    (and, with baseline=True, times the oracle as the CPU baseline)."""
+    import torch
+    from bf16_fp8_weight_amd import workloads as W
+    from bf16_fp8_weight_amd import wt
+
     t0 = time.time()
-    if args.workload == "mla_many_small_device":
+    if name == "mla_many_small_device":
         wl = W.mla_many_small(device="cuda", host=False)
     else:
-        wl = W.WORKLOADS[args.workload](device="cuda")
+        wl = W.WORKLOADS[name](device="cuda")
     torch.cuda.synchronize()
     log(f"workload {wl.name}: {len(wl.outputs)} outputs, {wl.input_bytes / 1e9:.3f} GB BF16 in, "
         f"{wl.n_tiles} tiles, generated in {time.time() - t0:.1f}s")
@@ -110,64 +169,55 @@ def main() -> int:
         ends[i].record(stream)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_begin
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    med_launch_ms = launch_ms[len(launch_ms) // 2] if len(launch_ms) % 2 else \
+        (launch_ms[len(launch_ms) // 2 - 1] + launch_ms[len(launch_ms) // 2]) / 2
     ms_per_step = t_total / args.steps * 1e3
 
     in_bytes = wl.input_bytes
     alg_bytes = wl.algorithmic_bytes
     value = in_bytes / (t_total / args.steps) / 1e9          # prepared BF16 GB/s, whole job
     achieved = alg_bytes / avg_launch_s / 1e9                # algorithmic HBM GB/s of the launch
-    log(f"steps {args.steps}: {ms_per_step:.4f} ms/step wall, launch avg {avg_launch_s * 1e3:.4f} ms "
-        f"(min {min(launch_ms):.4f}, max {max(launch_ms):.4f}); prepared {value:.1f} GB/s; "
+    log(f"{wl.name} steps {args.steps}: {ms_per_step:.4f} ms/step wall, launch avg {avg_launch_s * 1e3:.4f} ms "
+        f"(median {med_launch_ms:.4f}, min {launch_ms[0]:.4f}, max {launch_ms[-1]:.4f}); prepared {value:.1f} GB/s; "
         f"HBM {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.3f} of peak")
 
-    pipeline = None
+    out = {"_wl": wl}
     if wl.shard_mem == "host":
-        pipeline = _h2d_ceiling(wl, ms_per_step, args.steps)
-    if info["n_units"] > 1:
-        pipeline = pipeline or {}
-        pipeline["progress"] = _progress_timeline(plan, info["n_units"], sp)
+        out["pipeline"] = _h2d_ceiling(wl, ms_per_step, args.steps)
+    if progress and info["n_units"] > 1:
+        out.setdefault("pipeline", {})["progress"] = _progress_timeline(plan, info["n_units"], sp)
 
     traffic = None
-    try:
-        with open(args.traffic_json) as f:
-            tj = json.load(f)
-        if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha():
-            traffic = tj.get("bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    if traffic_json:
+        try:
+            with open(traffic_json) as f:
+                tj = json.load(f)
+            if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha():
+                traffic = tj.get("bytes_per_launch")
+        except (OSError, ValueError):
+            pass
 
-    cpu = None
-    verified = None
+    cpu, verified = None, None
     if not args.no_cpu_baseline:
-        cpu, verified = _cpu_baseline(wl, dst, args.cpu_threads)
+        cpu, verified = _verify(wl, dst, args.cpu_threads, baseline=baseline)
+    plan.close()
 
-    line = {
-        "metric": "prepared BF16 GB/s (shard gather+fuse+FP8 quant+pack) and % of HBM peak",
+    out.update({
         "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic: seeded N(0, 0.02) BF16, random weights of the stated shapes",
         "config": {
             "workload": wl.name,
             "outputs": len(wl.outputs),
             "input_bytes": in_bytes,
             "output_bytes": wl.output_bytes,
             "tiles": wl.n_tiles,
-            "shards_per_tensor": 8,
+            "shards_per_tensor": _shards_per_tensor(wl),
             "dst_mode": f"{args.dst_mode}, {args.dst_kind} destination, {wl.shard_mem}-resident shards",
         },
-        "pct_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
         "roofline": {
-            "bound": "hbm",
+            "bound": "h2d" if wl.shard_mem == "host" else "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -175,16 +225,19 @@ def main() -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(avg_launch_s * 1e3, 5),
+            "median_launch_ms": round(med_launch_ms, 5),
+            "min_launch_ms": round(launch_ms[0], 5),
             "launches_per_step": info["n_launches"],
         },
         "cpu_baseline": cpu,
         "verified_vs_oracle": verified,
-    }
-    if pipeline is not None:
-        line["pipeline"] = pipeline
-    print(json.dumps(line), flush=True)
-    plan.close()
-    return 0 if verified in (None, True) else 1
+    })
+    if wl.shard_mem == "host":
+        # bound by the host link: the fraction that matters is the overlap with a bare copy
+        out["roofline"]["frac_note"] = "HBM fraction of a host-link-bound replay; see pipeline.overlap_eff"
+    del dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def _h2d_ceiling(wl, ms_per_step: float, steps: int) -> dict:
@@ -268,9 +321,31 @@ def _kernel_sha() -> str:
     return kernel_sha()
 
 
-def _cpu_baseline(wl, dst, threads):
-    """Times the oracle over the whole workload on the host's cores (threads
-    over outputs) and compares its image with the GPU's output."""
+def _cpu_info() -> dict:
+    """The host's CPU: model name, logical cores, and the cores this process
+    may use (its affinity mask). One GPU's share of a GPU machine is 16 threads."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "machine_cores": os.cpu_count(), "usable_cores": usable}
+
+
+def _verify(wl, dst, threads: int, baseline: bool = True):
+    """Runs the oracle over the whole workload on the host, one thread per
+    output on the CPU share (min(16, usable cores) threads unless given), and
+    compares its image with the GPU's destination byte for byte. With
+    baseline=True it also reports that run as the CPU baseline, next to a
+    single-threaded run of the oracle over a bounded sample of the outputs."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -280,7 +355,8 @@ def _cpu_baseline(wl, dst, threads):
     import oracle_glue
 
     oracle.build(force=False)
-    n = threads or min(16, os.cpu_count() or 1)
+    ci = _cpu_info()
+    n = threads or max(1, min(16, ci["usable_cores"]))
     t0 = time.time()
     outs = oracle_glue.oracle_outputs(wl)  # D2H of the shard bytes (not timed)
     log(f"cpu baseline: copied {wl.input_bytes / 1e9:.2f} GB of shards to host in {time.time() - t0:.1f}s")
@@ -291,15 +367,39 @@ def _cpu_baseline(wl, dst, threads):
     dt = time.perf_counter() - t1
     got = dst.cpu().numpy()
     ok = bool(np.array_equal(got, img))
-    log(f"cpu baseline: oracle {dt:.2f}s on {n} threads = {wl.input_bytes / dt / 1e9:.3f} GB/s; GPU output "
+    del got
+    log(f"{wl.name}: oracle {dt:.2f}s on {n} threads = {wl.input_bytes / dt / 1e9:.3f} GB/s; GPU output "
         f"{'identical to' if ok else 'DIFFERS from'} the oracle image")
+    if not baseline:
+        return None, ok
+    # single thread: the outputs in table order until 512 MB of BF16 input
+    # (or all of them), into a scratch image
+    in_bytes = [sum(p.rows for p in o.parts) * o.cols * 2 for o in wl.outputs]
+    k, acc = 0, 0
+    while k < len(outs) and acc < (512 << 20):
+        acc += in_bytes[k]
+        k += 1
+    scratch = np.zeros(wl.dst_bytes, dtype=np.uint8)
+    t2 = time.perf_counter()
+    oracle.prepare(outs[:k], wl.dst_bytes, scratch)
+    dt1 = time.perf_counter() - t2
+    log(f"{wl.name}: oracle single-threaded {dt1:.2f}s over {k} outputs ({acc / 1e9:.3f} GB) = "
+        f"{acc / dt1 / 1e9:.3f} GB/s; CPU {ci['cpu_model']}, {ci['machine_cores']} logical cores, "
+        f"{ci['usable_cores']} usable")
     return {
         "value": round(wl.input_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": n,
         "kind": "oracle",
-        "sample": f"the whole workload ({len(outs)} outputs, {wl.input_bytes} B BF16), one thread per output",
+        "sample": f"the whole workload ({len(outs)} outputs, {wl.input_bytes} B BF16), one thread per output "
+                  f"on {n} threads",
         "seconds": round(dt, 2),
+        "threads": n,
+        "all_cores_GBps": round(wl.input_bytes / dt / 1e9, 4),
+        "single_thread_GBps": round(acc / dt1 / 1e9, 4),
+        "single_thread_sample": f"the first {k} outputs in table order ({acc} B BF16), one thread",
+        "single_thread_seconds": round(dt1, 2),
+        **ci,
     }, ok
 
 
@@ -406,7 +506,8 @@ def _bench_act(args) -> int:
             gq, gs = qt.cpu().numpy().reshape(n_out, H), st.cpu().numpy().reshape(n_out, 4 * nb)
         verified = bool(np.array_equal(gq, wq) and np.array_equal(gs, ws))
         cpu = {"value": round(wl.input_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"the whole workload ({n_out} rows x {H}), one thread", "seconds": round(dt, 3)}
+               "sample": f"the whole workload ({n_out} rows x {H}), one thread", "seconds": round(dt, 3),
+               "threads": 1, "single_thread_GBps": round(wl.input_bytes / dt / 1e9, 4), **_cpu_info()}
         log(f"cpu baseline: oracle {dt:.3f}s; GPU output {'identical to' if verified else 'DIFFERS from'} the oracle")
 
     line = {

@@ -143,22 +143,24 @@ wt_status check_memory(const void *p, uint64_t bytes, int32_t kind, int device, 
       *err = what + ": device memory of another GPU";
       return WT_E_INVAL;
     }
-    hipDeviceptr_t base = nullptr;
-    size_t size = 0;
-    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) == hipSuccess && base) {
-      const uint64_t lo = (uint64_t)(uintptr_t)base, hi = lo + size;
-      if ((uint64_t)(uintptr_t)p + bytes > hi) {
-        *err = what + ": range runs past the end of its allocation";
-        return WT_E_RANGE;
-      }
-    } else {
-      (void)hipGetLastError();
-    }
   } else {
     if (a.type != hipMemoryTypeHost) {
       *err = what + ": expected pinned host memory";
       return WT_E_INVAL;
     }
+  }
+  // extent: the allocation that holds p must also hold p + bytes - 1 (device
+  // allocations and pinned host allocations alike are tracked by the runtime)
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) == hipSuccess && base) {
+    const uint64_t lo = (uint64_t)(uintptr_t)base, hi = lo + size;
+    if ((uint64_t)(uintptr_t)p < lo || (uint64_t)(uintptr_t)p + bytes > hi) {
+      *err = what + ": range runs past the end of its allocation";
+      return WT_E_RANGE;
+    }
+  } else {
+    (void)hipGetLastError();
   }
   return WT_OK;
 }

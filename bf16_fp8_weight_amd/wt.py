@@ -406,9 +406,14 @@ def task_table(wl, group_base: int = 0) -> TaskTable:
 
 
 class Plan:
-    """Owns a wt_plan handle for a workload and a destination tensor."""
+    """Owns a wt_plan handle for a workload and a destination tensor.
+
+    The plan holds the shards' and the destination's addresses, so it keeps
+    the workload (and with it every shard tensor and the pinned arena) and the
+    destination tensor alive until it is closed."""
 
     def __init__(self, wl, dst, dst_kind: int = WT_MEM_DEVICE, opts: Optional[wt_plan_options] = None):
+        self.wl = wl
         self.table = task_table(wl)
         self.dst = dst
         self.handle = wt_plan_create(self.table, dst.data_ptr(), dst.numel() * dst.element_size(), dst_kind, opts)
@@ -423,6 +428,8 @@ class Plan:
         if self.handle:
             wt_plan_destroy(self.handle)
             self.handle = 0
+        self.wl = None
+        self.dst = None
 
     def __enter__(self) -> "Plan":
         return self

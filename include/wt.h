@@ -192,7 +192,10 @@ wt_status wt_plan_check(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, 
 wt_status wt_plan_schedule(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, int32_t dst_kind,
                            const wt_plan_options *opts, wt_sched_op *ops, size_t max_ops, size_t *n_ops);
 
-/* Builds a plan (the static schedule, computed once): validates the table,
+/* Builds a plan: the static schedule of "Weight transfer for RL post-training
+ * in under 2 seconds", section "Static schedule" (the transfer schedule is
+ * computed once at initialisation and every training step replays it). It
+ * validates the table,
  * builds the device descriptor tables (outputs, row segments, tile and copy
  * work lists), allocates staging within the watermark and creates the
  * plan's streams and events. The table is copied; the caller may free it on
@@ -204,7 +207,11 @@ wt_status wt_plan_schedule(const wt_task *tasks, size_t n_tasks, size_t dst_byte
 wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
                          const wt_plan_options *opts, wt_plan **out);
 
-/* Replays the plan: enqueues the whole preparation so that it is ordered
+/* Replays the plan (same page, section "Static schedule": each iteration
+ * replays the schedule; section "Task pipeline": per task, the stages
+ * parameter preparation -> RDMA transfer, each with its own FIFO queue, a
+ * task moving to the next queue once its stage is done). Enqueues the whole
+ * preparation so that it is ordered
  * after prior work on `stream` and completes before later work on `stream`.
  * With device-resident shards and WT_DST_ZERO_COPY this is one kernel launch
  * on `stream`. Pinned-host shards or WT_DST_STAGED run the three-stage
@@ -219,17 +226,25 @@ wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t
  * capture (its launches, completion-word kernels and event record become
  * graph nodes; each graph replay is a replay of the plan); a pipelined plan
  * may not, since its backpressure waits on the host (WT_E_STATE, nothing
- * enqueued). Returns WT_E_STATE if another wt_prepare on the same plan is
+ * enqueued). A graph holding captured replays reads the plan's device
+ * tables every time it is launched: it must not be launched after
+ * wt_plan_destroy, and its launches must have finished before that call.
+ * Returns WT_E_STATE if another wt_prepare on the same plan is
  * running in another thread, WT_E_HIP on a runtime error. */
 wt_status wt_prepare(wt_plan *plan, void *stream);
 
 /* Copies the plan's shape into *info. */
 wt_status wt_plan_get_info(const wt_plan *plan, wt_plan_info *info);
 
-/* Waits for the plan's work already enqueued (its own streams, and for a
- * plan without a pipeline the latest launch on the caller's stream), then
- * frees everything the plan owns (device tables, staging, streams, events).
- * Never frees shards or the destination region. NULL is ignored. */
+/* Ends a plan. The staging it frees is the temporary memory that the
+ * watermark bounds ("Weight transfer for RL post-training in under 2
+ * seconds", section "GPU memory usage control"). Waits for the plan's work
+ * already enqueued (its own streams, and for a plan without a pipeline the
+ * latest wt_prepare launch on the caller's stream), then frees everything
+ * the plan owns (device tables, staging, streams, events). Launches of a
+ * captured graph are not waited for: every graph holding replays of this
+ * plan must have finished, and must not be launched again, before this
+ * call. Never frees shards or the destination region. NULL is ignored. */
 void wt_plan_destroy(wt_plan *plan);
 
 /* Static text for a status code. */

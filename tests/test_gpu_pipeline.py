@@ -136,3 +136,37 @@ def test_create_rejects_bad_memory(wt):
     with pytest.raises(wt.WtError) as e:
         wt.wt_plan_create(tab, dst.data_ptr(), wl.dst_bytes)
     assert e.value.status == wt.WT_E_INVAL
+
+
+def test_create_rejects_pinned_host_ranges_past_their_allocation(wt):
+    # pinned-host destination and pinned-host shards are checked against the
+    # extent of their allocation like device memory: refused at create time,
+    # before any kernel runs. Two 1 MiB pinned allocations of exactly known
+    # size from the HIP runtime.
+    import ctypes
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+    hip.hipHostFree.argtypes = [ctypes.c_void_p]
+    size = 1 << 20
+    bufs = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for b in bufs:
+        assert hip.hipHostMalloc(ctypes.byref(b), size, 0) == 0
+    try:
+        dst, src = bufs[0].value, bufs[1].value
+        wl = W.custom([(64, 128)], n_shards=1, device="cpu")
+        tab = wt.task_table(wl)
+        tab.arr[0].shard_mem = wt.WT_MEM_PINNED_HOST
+        tab.arr[0].shards[0].ptr = src
+        wt.wt_plan_destroy(wt.wt_plan_create(tab, dst, wl.dst_bytes, wt.WT_MEM_PINNED_HOST))
+        with pytest.raises(wt.WtError) as e:
+            wt.wt_plan_create(tab, dst, size + 65536, wt.WT_MEM_PINNED_HOST)
+        assert e.value.status == wt.WT_E_RANGE
+        # 64 rows of 256 bytes starting 4 KiB before the end of the allocation
+        tab.arr[0].shards[0].ptr = src + size - 4096
+        with pytest.raises(wt.WtError) as e:
+            wt.wt_plan_create(tab, dst, wl.dst_bytes, wt.WT_MEM_PINNED_HOST)
+        assert e.value.status == wt.WT_E_RANGE
+    finally:
+        for b in bufs:
+            hip.hipHostFree(b)

@@ -346,3 +346,29 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import bf16_fp8_weight_amd.wt"], capture_output=True, text=True,
                        timeout=120, cwd=ROOT, env=env)
     assert r.returncode != 0 and "ImportError" in r.stderr
+
+
+def test_plan_keeps_shards_and_destination_alive(wt, monkeypatch):
+    # a Plan holds raw shard and destination addresses: the workload's shard
+    # tensors and the destination must live as long as the plan does, even
+    # when the caller drops its own references
+    import gc
+    import weakref
+
+    import torch
+
+    wl = W.custom([(5, 7), (3, 7)], device="cpu")
+    shard_refs = [weakref.ref(s) for o in wl.outputs for p in o.parts for s in p.shards]
+    dst = torch.empty(wl.dst_bytes, dtype=torch.uint8)
+    dst_ref = weakref.ref(dst)
+    destroyed = []
+    monkeypatch.setattr(wt, "wt_plan_create", lambda *a, **k: 12345)
+    monkeypatch.setattr(wt, "wt_plan_destroy", lambda h: destroyed.append(h))
+    plan = wt.Plan(wl, dst)
+    del wl, dst
+    gc.collect()
+    assert all(r() is not None for r in shard_refs) and dst_ref() is not None
+    plan.close()
+    assert destroyed == [12345]
+    gc.collect()
+    assert all(r() is None for r in shard_refs) and dst_ref() is None
