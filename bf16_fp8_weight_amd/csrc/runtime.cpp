@@ -61,6 +61,10 @@ struct wt_plan {
   uint64_t replays = 0;             // pipelined replays enqueued so far
 
   std::vector<char> rel_waited;  // per chunk: some later chunk waits for its release
+  // no-allocation plan (wt_plan_create_noalloc): its device tables live in
+  // the device's static scratch array and ev_last is that device's event;
+  // neither is freed by the plan
+  struct NoAllocDev *noalloc = nullptr;
   std::atomic<bool> busy{false};
   mutable std::mutex err_mu;
   std::string last_error;
@@ -112,6 +116,54 @@ struct DeviceGuard {
     if (ok) (void)hipSetDevice(prev);
   }
 };
+
+}  // namespace
+
+// ---- device tables without allocation (wt_plan_create_noalloc)
+// One static array per GPU holds the descriptor tables of that GPU's one
+// no-allocation plan. On the host, `scratch` names a host-side stand-in,
+// not device memory: host code uses only the device address that
+// hipGetSymbolAddress returns for it (per device, at the first
+// no-allocation call on that device).
+static __device__ __align__(256) uint8_t scratch[WT_NOALLOC_TABLE_BYTES];
+
+struct NoAllocDev {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  uint8_t *ptr = nullptr;   // this device's copy of `scratch`
+  hipEvent_t ev = nullptr;  // after the latest replay of the device's no-allocation plan
+  std::atomic<bool> in_use{false};
+};
+
+namespace {
+
+constexpr int kMaxNoAllocDevices = 64;
+NoAllocDev g_noalloc[kMaxNoAllocDevices];
+
+// Set-up of device `dev` (which must be current): the address of its scratch
+// array and its event, made once per device and kept until the process ends.
+NoAllocDev *noalloc_device(int dev, std::string *err) {
+  if (dev < 0 || dev >= kMaxNoAllocDevices) {
+    *err = "device ordinal out of range for the no-allocation path";
+    return nullptr;
+  }
+  NoAllocDev &d = g_noalloc[dev];
+  std::call_once(d.once, [&d] {
+    void *a = nullptr;
+    d.err = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (d.err == hipSuccess && !a) d.err = hipErrorInvalidSymbol;
+    if (d.err == hipSuccess) {
+      d.ptr = (uint8_t *)a;
+      d.err = hipEventCreateWithFlags(&d.ev, hipEventDisableTiming);
+    }
+    if (d.err != hipSuccess) (void)hipGetLastError();
+  });
+  if (d.err != hipSuccess) {
+    *err = hip_msg("no-allocation set-up (hipGetSymbolAddress / hipEventCreate)", d.err);
+    return nullptr;
+  }
+  return &d;
+}
 
 wt_plan_options resolve_opts(const wt_plan_options *o) {
   wt_plan_options d;
@@ -192,6 +244,12 @@ size_t blob_bytes(const std::vector<T> &v) {
 
 void destroy_resources(wt_plan *p) {
   if (p->ev_last) (void)hipEventSynchronize(p->ev_last);  // the tables are in use until then
+  if (p->noalloc) {
+    // the event and the scratch array belong to the device, not the plan
+    p->ev_last = nullptr;
+    p->noalloc->in_use.store(false);
+    p->noalloc = nullptr;
+  }
   if (p->s_prep) (void)hipStreamSynchronize(p->s_prep);
   if (p->s_out) (void)hipStreamSynchronize(p->s_out);
   if (p->s_h2d) (void)hipStreamSynchronize(p->s_h2d);
@@ -232,6 +290,11 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
   }
   const Layout &L = p->L;
   p->pipeline = !L.chunks.empty();
+  if (p->noalloc && (p->pipeline || L.staging_bytes > 0)) {
+    set_err(p, "pinned-host shards and staged writes need staging memory, which a plan without allocation "
+               "cannot have");
+    return WT_E_INVAL;
+  }
 
   if (L.staging_bytes > 0) HIP_OR(p, hipMalloc((void **)&p->staging, (size_t)L.staging_bytes));
 
@@ -259,14 +322,25 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
              blob_bytes(t.general) + blob_bytes(t.copies);
   const size_t epoch_off = total;
   total += 256;
-  std::vector<uint8_t> blob(total, 0);
-  HIP_OR(p, hipMalloc((void **)&p->tables, total));
+  std::vector<uint8_t> blob(total, 0);  // zero-filled: the replay counter starts at 0
+  uint8_t *base = nullptr;
+  if (p->noalloc) {
+    if (total > (size_t)WT_NOALLOC_TABLE_BYTES) {
+      set_err(p, "device tables need " + std::to_string(total) + " bytes, above the " +
+                     std::to_string((size_t)WT_NOALLOC_TABLE_BYTES) + " bytes a plan without allocation can hold");
+      return WT_E_NOMEM;
+    }
+    base = p->noalloc->ptr;
+  } else {
+    HIP_OR(p, hipMalloc((void **)&p->tables, total));
+    base = p->tables;
+  }
   size_t off = 0;
   for (const HostTables &t : hts) {
     LaunchTables T{};
     auto put = [&](const auto &v) -> uint64_t {
       using E = typename std::decay_t<decltype(v)>::value_type;
-      const uint64_t dev = (uint64_t)(uintptr_t)(p->tables + off);
+      const uint64_t dev = (uint64_t)(uintptr_t)(base + off);
       if (!v.empty()) std::memcpy(blob.data() + off, v.data(), v.size() * sizeof(E));
       off += blob_bytes(v);
       return dev;
@@ -288,10 +362,13 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
     T.n_copies = (uint32_t)t.copies.size();
     p->batches.push_back(T);
   }
-  p->epoch = (uint64_t *)(p->tables + epoch_off);
-  HIP_OR(p, hipMemcpy(p->tables, blob.data(), total, hipMemcpyHostToDevice));
+  p->epoch = (uint64_t *)(base + epoch_off);
+  HIP_OR(p, hipMemcpy(base, blob.data(), total, hipMemcpyHostToDevice));
 
-  if (!p->pipeline) HIP_OR(p, hipEventCreateWithFlags(&p->ev_last, hipEventDisableTiming));
+  if (p->noalloc)
+    p->ev_last = p->noalloc->ev;
+  else if (!p->pipeline)
+    HIP_OR(p, hipEventCreateWithFlags(&p->ev_last, hipEventDisableTiming));
   if (p->pipeline) {
     HIP_OR(p, hipStreamCreateWithFlags(&p->s_h2d, hipStreamNonBlocking));
     HIP_OR(p, hipStreamCreateWithFlags(&p->s_prep, hipStreamNonBlocking));
@@ -466,8 +543,8 @@ wt_status wt_plan_schedule(const wt_task *tasks, size_t n_tasks, size_t dst_byte
   }
 }
 
-wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
-                         const wt_plan_options *opts, wt_plan **out) {
+static wt_status plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
+                             const wt_plan_options *opts, bool noalloc, wt_plan **out) {
   if (!out) return WT_E_INVAL;
   *out = nullptr;
   wt_plan *p = nullptr;
@@ -499,6 +576,22 @@ wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t
     p->dst_bytes = dst_bytes;
     p->dst_kind = dst_kind;
     DeviceGuard guard(dev);
+    if (noalloc) {
+      NoAllocDev *d = noalloc_device(dev, &err);
+      if (!d) {
+        set_err(nullptr, err);
+        delete p;
+        return WT_E_HIP;
+      }
+      bool expected = false;
+      if (!d->in_use.compare_exchange_strong(expected, true)) {
+        set_err(nullptr, "another plan without allocation is live on device " + std::to_string(dev) +
+                             " (one per device: its tables occupy the device's scratch array)");
+        delete p;
+        return WT_E_STATE;
+      }
+      p->noalloc = d;
+    }
     st = create_impl(p, tasks, n_tasks, o);
     if (st != WT_OK) {
       set_err(nullptr, p->last_error);
@@ -523,6 +616,16 @@ wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t
     }
     return WT_E_INVAL;
   }
+}
+
+wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
+                         const wt_plan_options *opts, wt_plan **out) {
+  return plan_create(tasks, n_tasks, dst, dst_bytes, dst_kind, opts, false, out);
+}
+
+wt_status wt_plan_create_noalloc(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
+                                 const wt_plan_options *opts, wt_plan **out) {
+  return plan_create(tasks, n_tasks, dst, dst_bytes, dst_kind, opts, true, out);
 }
 
 wt_status wt_prepare(wt_plan *plan, void *stream) {

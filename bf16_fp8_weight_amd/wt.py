@@ -33,6 +33,7 @@ EXPORTS = [
     "wt_quantize_domain", "wt_cast_f32_range",
     "wt_schedule_build", "wt_schedule_info", "wt_schedule_output", "wt_schedule_tasks", "wt_schedule_destroy",
     "wt_plan_set_progress", "wt_plan_task_unit", "wt_progress_wait", "wt_quantize_act_b128",
+    "wt_plan_create_noalloc",
 ]
 
 
@@ -128,6 +129,8 @@ def _load() -> ctypes.CDLL:
     L.wt_plan_schedule.argtypes = [P(wt_task), sz, sz, i32, P(wt_plan_options), P(wt_sched_op), sz, P(sz)]
     L.wt_plan_create.restype = ctypes.c_int
     L.wt_plan_create.argtypes = [P(wt_task), sz, vp, sz, i32, P(wt_plan_options), P(vp)]
+    L.wt_plan_create_noalloc.restype = ctypes.c_int
+    L.wt_plan_create_noalloc.argtypes = [P(wt_task), sz, vp, sz, i32, P(wt_plan_options), P(vp)]
     L.wt_prepare.restype = ctypes.c_int
     L.wt_prepare.argtypes = [vp, vp]
     L.wt_plan_get_info.restype = ctypes.c_int
@@ -245,6 +248,14 @@ def wt_plan_create(table: TaskTable, dst_ptr: int, dst_bytes: int, dst_kind: int
     out = ctypes.c_void_p(0)
     _check(lib.wt_plan_create(table.arr, table.n, dst_ptr, dst_bytes, dst_kind,
                               ctypes.byref(opts) if opts else None, ctypes.byref(out)))
+    return out.value
+
+
+def wt_plan_create_noalloc(table: TaskTable, dst_ptr: int, dst_bytes: int, dst_kind: int = WT_MEM_DEVICE,
+                           opts: Optional[wt_plan_options] = None) -> int:
+    out = ctypes.c_void_p(0)
+    _check(lib.wt_plan_create_noalloc(table.arr, table.n, dst_ptr, dst_bytes, dst_kind,
+                                      ctypes.byref(opts) if opts else None, ctypes.byref(out)))
     return out.value
 
 

@@ -207,6 +207,31 @@ wt_status wt_plan_schedule(const wt_task *tasks, size_t n_tasks, size_t dst_byte
 wt_status wt_plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
                          const wt_plan_options *opts, wt_plan **out);
 
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): builds the same plan
+ * as wt_plan_create, with the same arguments, validation and results, but
+ * calls no hipMalloc, hipHostMalloc or hipFree (host-side bookkeeping uses
+ * the C++ heap). Its device descriptor tables go into a static array of
+ * WT_NOALLOC_TABLE_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends; they are copied there synchronously before
+ * the call returns. Limits:
+ *  - one such plan per device at a time: while one is live on the device,
+ *    another call returns WT_E_STATE (destroy the first with
+ *    wt_plan_destroy, which waits for its latest wt_prepare launch);
+ *  - tables larger than WT_NOALLOC_TABLE_BYTES (16 MiB): WT_E_NOMEM. A pair
+ *    of full 128 x 128 tiles takes 32 bytes of tables, so 16 MiB holds, for
+ *    example, a dense 7B-shaped model (about 6.5 MB of tables);
+ *  - pinned-host shards or WT_DST_STAGED (they need staging memory):
+ *    WT_E_INVAL.
+ * Replays, progress words and destruction work as for any plan. A plan
+ * created here shares the device's array with every later one: a graph that
+ * captured its replays must not be launched after it is destroyed, and work
+ * of an earlier plan that still reads the array when a new plan is created
+ * (graph launches are not tracked) races with it. */
+#define WT_NOALLOC_TABLE_BYTES 16777216u
+wt_status wt_plan_create_noalloc(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes,
+                                 int32_t dst_kind, const wt_plan_options *opts, wt_plan **out);
+
 /* Replays the plan (same page, section "Static schedule": each iteration
  * replays the schedule; section "Task pipeline": per task, the stages
  * parameter preparation -> RDMA transfer, each with its own FIFO queue, a
