@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libwt.so")
 
-SOURCES = ["plan.cpp", "schedule.cpp", "runtime.cpp", "prep_kernels.hip", "progress.hip", "act_quant.hip"]
+SOURCES = ["plan.cpp", "schedule.cpp", "host_api.cpp", "runtime.cpp", "prep_kernels.hip", "progress.hip", "act_quant.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

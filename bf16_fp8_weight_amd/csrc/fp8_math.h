@@ -124,12 +124,18 @@ __device__ __forceinline__ float qdiv(float x, const TileQ &t) {
   return x / t.s;
 }
 
-// Saturation to [-448, 448] before the hardware convert (v_cvt_pk_fp8_f32
-// rounds to nearest even but does not saturate, and takes no clamp modifier).
-// On this path every quotient is at most 448.88 in magnitude, below 464, so
-// the clamp never changes a byte; it keeps the cast saturating by
-// construction.
+// Saturation to [-448, 448] (v_cvt_pk_fp8_f32 rounds to nearest even but
+// does not saturate: from 464 up it gives the NaN code, and it takes no clamp
+// modifier). Used by the standalone cast check (cast of any fp32 value).
 __device__ __forceinline__ float sat448(float q) { return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f); }
+
+// The element functions below convert without that clamp: a block's
+// quotients are |x| / s <= amax / s, at most 448.88 in magnitude for every
+// positive BF16 amax (448 exactly up to the rounding of s), and the convert
+// rounds every value below 464 to at most 448 (0x7E) on its own, so a clamp
+// could never change a byte. wt_quantize_domain runs exactly this code over
+// every (x, amax) pair of BF16 values with |x| <= amax, which is how the
+// claim is checked against the oracle's saturating cast.
 
 // Four BF16 (two packed words) -> four E4M3 bytes, little-endian in one word.
 template <bool Recip>
@@ -138,8 +144,8 @@ __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const TileQ
   const float c = qdiv<Recip>(bf16_lo(w1), t), d = qdiv<Recip>(bf16_hi(w1), t);
   // the first convert fills bytes 0-1 and keeps bytes 2-3 of its third
   // operand, which the second convert then overwrites: any register will do
-  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), (int)w1, false);
-  r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), (int)r, true);
+  uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w1, false);
+  r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
   return r;
 }
 
@@ -148,14 +154,14 @@ __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, const TileQ
 template <bool Recip>
 __device__ __forceinline__ uint32_t quant2(uint32_t w, const TileQ &t) {
   const float a = qdiv<Recip>(bf16_lo(w), t), b = qdiv<Recip>(bf16_hi(w), t);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), (int)w, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)w, false);
 }
 
 // One BF16 -> one E4M3 byte (same arithmetic as quant4, one lane).
 template <bool Recip>
 __device__ __forceinline__ uint32_t quant1(uint32_t xbits, const TileQ &t) {
   const float a = qdiv<Recip>(__uint_as_float(xbits << 16), t);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), 0.0f, 0, false) & 0xFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, 0.0f, 0, false) & 0xFFu;
 }
 
 }  // namespace wt

@@ -434,6 +434,13 @@ void build_tables(const Layout &L, const std::vector<int32_t> &outputs, const Ba
     }
     d.flags = fast ? kOutFast : 0;
     t->outs.push_back(d);
+    // a tile row is 256 bytes of BF16 and 128 of FP8: unless both row strides
+    // and both bases are multiples of 128 bytes, the first and last line of
+    // each tile row segment are shared with the neighbouring tiles
+    if (fast && (H.cols % 128 != 0 || d.q % 128 != 0)) t->xcd_order = true;
+    if (fast)
+      for (size_t s2 = 0; s2 < H.segs.size(); ++s2)
+        if (t->segs[seg_base + s2].src % 128 != 0) t->xcd_order = true;
     size_t s = 0;
     for (int64_t I = 0; I < H.tiles_r; ++I) {
       while (s + 1 < H.segs.size() && H.segs[s].row0 + H.segs[s].nrows <= I * kTile) ++s;

@@ -85,6 +85,7 @@ struct HostTables {
   std::vector<TileItem> edge;
   std::vector<GenDesc> general;
   std::vector<CopyItem> copies;
+  bool xcd_order = false;  // some aligned-path output's rows share 128-byte lines with a neighbour tile's
 };
 
 // Address resolver for one batch: where output k's inputs and outputs are.
@@ -106,5 +107,12 @@ void add_copy_items(std::vector<CopyItem> &v, uint64_t src, uint64_t dst, uint64
 
 // Records of the schedule one wt_prepare replays, in enqueue order.
 void schedule_ops(const Layout &L, std::vector<wt_sched_op> *ops);
+
+// Options with defaults filled in (host_api.cpp).
+wt_plan_options resolve_opts(const wt_plan_options *o);
+// The calling thread's last error text (host_api.cpp).
+void set_thread_error(const std::string &msg);
+// Text of the last error recorded on a plan (runtime.cpp).
+const char *plan_error_text(const wt_plan *plan);
 
 }  // namespace wt

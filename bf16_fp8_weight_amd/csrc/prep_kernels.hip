@@ -571,33 +571,6 @@ __device__ __forceinline__ void general_tile(const LaunchTables &T, const GenDes
 
 // ------------------------------------------------------------ kernels
 
-// Blocks [0, n_fast): one regular tile each; [n_fast, n_fast + n_edge): one
-// edge tile each; then TW copy items per block (one per wave). At most
-// WT_BLOCKS_PER_CU blocks per compute unit (dynamic-LDS request).
-template <bool Paced>
-__global__ __launch_bounds__(TT) void prep_fast_copy_kernel(LaunchTables T) {
-  __shared__ uint32_t red[4 * TW];
-  uint32_t b = blockIdx.x;
-  if (b < T.n_fast) {
-    const RegDesc x = ld_table(T.fast_tiles, b);
-    if (kGroupTiles >= 4 && (x.flags & kRegQuad))
-      group_tile<kGroupTiles >= 4 ? 4 : 2, Paced>(x, red);
-    else if (kGroupTiles >= 2 && (x.flags & kRegPair))
-      group_tile<2, Paced>(x, red);
-    else
-      reg_tile<Paced>(x, red);
-    return;
-  }
-  b -= T.n_fast;
-  if (b < T.n_edge) {
-    edge_tile<Paced>(T, b, red);
-    return;
-  }
-  b -= T.n_edge;
-  const uint32_t ci = b * TW + (threadIdx.x >> 6);
-  if (ci < T.n_copies) copy_item(ld_table(T.copies, ci), threadIdx.x & 63);
-}
-
 // Workgroup b of a launch goes to XCD b % 8 (round-robin dispatch), and each
 // XCD has its own L2. A general tile's rows start at any 2-byte alignment, so
 // the first and last 128-byte line of each row segment are shared with the
@@ -609,6 +582,33 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t n) {
   constexpr uint32_t kXcds = 8;
   const uint32_t per = n / kXcds, rem = n % kXcds, x = b % kXcds;
   return x * per + min(x, rem) + b / kXcds;
+}
+
+// Blocks [0, n_fast): one regular tile each; [n_fast, n_fast + n_edge): one
+// edge tile each; then TW copy items per block (one per wave). At most
+// WT_BLOCKS_PER_CU blocks per compute unit (dynamic-LDS request).
+template <bool Paced>
+__global__ __launch_bounds__(TT) void prep_fast_copy_kernel(LaunchTables T) {
+  __shared__ uint32_t red[4 * TW];
+  uint32_t b = blockIdx.x;
+  if (b < T.n_fast) {
+    const RegDesc x = ld_table(T.fast_tiles, T.xcd_order ? xcd_contiguous(b, T.n_fast) : b);
+    if (kGroupTiles >= 4 && (x.flags & kRegQuad))
+      group_tile<kGroupTiles >= 4 ? 4 : 2, Paced>(x, red);
+    else if (kGroupTiles >= 2 && (x.flags & kRegPair))
+      group_tile<2, Paced>(x, red);
+    else
+      reg_tile<Paced>(x, red);
+    return;
+  }
+  b -= T.n_fast;
+  if (b < T.n_edge) {
+    edge_tile<Paced>(T, T.xcd_order ? xcd_contiguous(b, T.n_edge) : b, red);
+    return;
+  }
+  b -= T.n_edge;
+  const uint32_t ci = b * TW + (threadIdx.x >> 6);
+  if (ci < T.n_copies) copy_item(ld_table(T.copies, ci), threadIdx.x & 63);
 }
 
 __global__ __launch_bounds__(GT) void prep_general_kernel(LaunchTables T) {
@@ -676,15 +676,11 @@ struct FastLaunchParams {
   uint32_t lds = 0, one_round = 0;
 };
 
-static FastLaunchParams fast_launch_params() {
+static FastLaunchParams fast_launch_params(int dev) {
   constexpr int kMaxDevices = 64;
   static FastLaunchParams cache[kMaxDevices];
   static std::once_flag once[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return FastLaunchParams{};
-  }
+  if (dev < 0 || dev >= kMaxDevices) return FastLaunchParams{};
   std::call_once(once[dev], [dev] {
     FastLaunchParams p;
     int lds_cu = 0, lds_blk = 0, cus = 0;
@@ -702,12 +698,13 @@ static FastLaunchParams fast_launch_params() {
   return cache[dev];
 }
 
-hipError_t launch_batch(const LaunchTables &T, hipStream_t stream) {
+// `device` is the current device (the plan's).
+hipError_t launch_batch(const LaunchTables &T, hipStream_t stream, int device) {
   const uint64_t copy_blocks = (T.n_copies + TW - 1) / TW;
   const uint64_t blocks = (uint64_t)T.n_fast + T.n_edge + copy_blocks;
   if (blocks > 0) {
     if (blocks > UINT32_MAX / TT) return hipErrorInvalidValue;
-    const FastLaunchParams lp = fast_launch_params();
+    const FastLaunchParams lp = fast_launch_params(device);
     // Measured on MI355X, one dense layer of hidden size 1024 (720 tiles,
     // one round of workgroups): 15.5 us per launch paced, 14.2 unpaced.
     if (blocks <= lp.one_round)

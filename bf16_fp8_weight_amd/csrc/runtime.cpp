@@ -26,13 +26,12 @@
 #include "wt.h"
 
 namespace wt {
-hipError_t launch_batch(const LaunchTables &T, hipStream_t stream);
+hipError_t launch_batch(const LaunchTables &T, hipStream_t stream, int device);
 hipError_t launch_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, uint8_t *out, int variant,
                                   hipStream_t stream);
 hipError_t launch_cast_range(uint32_t first, uint64_t count, uint8_t *out, hipStream_t stream);
-hipError_t launch_progress_begin(uint64_t *epoch, hipStream_t stream);
 hipError_t launch_act_quant(const ActArgs &a, bool fast, hipStream_t stream);
-hipError_t launch_progress_mark(const uint64_t *epoch, uint64_t *word, hipStream_t stream);
+hipError_t launch_progress_mark(uint64_t *epoch, uint64_t *word, bool first, hipStream_t stream);
 }  // namespace wt
 
 using namespace wt;
@@ -72,21 +71,24 @@ struct wt_plan {
 
 namespace {
 
-thread_local std::string g_last_error;
-
 void set_err(wt_plan *p, const std::string &m) {
   if (p) {
     std::lock_guard<std::mutex> g(p->err_mu);
     p->last_error = m;
   } else {
-    g_last_error = m;
+    set_thread_error(m);
   }
 }
 
 }  // namespace
 
 namespace wt {
-void set_thread_error(const std::string &msg) { g_last_error = msg; }
+// Text of the last error recorded on a plan (wt_plan_last_error).
+const char *plan_error_text(const wt_plan *plan) {
+  std::lock_guard<std::mutex> g(plan->err_mu);
+  // the string lives in the plan; valid until the next error on it or destroy
+  return plan->last_error.c_str();
+}
 }  // namespace wt
 
 namespace {
@@ -104,16 +106,20 @@ std::string hip_msg(const char *what, hipError_t e) {
     }                                                    \
   } while (0)
 
-// Restores the caller's current device on scope exit.
+// Makes `dev` current for the scope and restores the caller's device on
+// exit; a no-op (one hipGetDevice) when `dev` is current already.
 struct DeviceGuard {
   int prev = -1;
-  bool ok = false;
+  bool switched = false;
   explicit DeviceGuard(int dev) {
-    if (hipGetDevice(&prev) == hipSuccess) ok = true;
-    if (dev >= 0 && dev != prev) (void)hipSetDevice(dev);
+    if (hipGetDevice(&prev) != hipSuccess) {
+      (void)hipGetLastError();
+      prev = -1;
+    }
+    if (dev >= 0 && dev != prev && hipSetDevice(dev) == hipSuccess) switched = prev >= 0;
   }
   ~DeviceGuard() {
-    if (ok) (void)hipSetDevice(prev);
+    if (switched) (void)hipSetDevice(prev);
   }
 };
 
@@ -163,15 +169,6 @@ NoAllocDev *noalloc_device(int dev, std::string *err) {
     return nullptr;
   }
   return &d;
-}
-
-wt_plan_options resolve_opts(const wt_plan_options *o) {
-  wt_plan_options d;
-  wt_plan_options_init(&d);
-  if (!o) return d;
-  wt_plan_options r = *o;
-  if (r.watermark_bytes == 0) r.watermark_bytes = d.watermark_bytes;
-  return r;
 }
 
 // Checks that [p, p + bytes) lies in one allocation of the expected kind.
@@ -360,6 +357,7 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
     T.n_edge = (uint32_t)t.edge.size();
     T.n_general = (uint32_t)t.general.size();
     T.n_copies = (uint32_t)t.copies.size();
+    T.xcd_order = t.xcd_order ? 1u : 0u;
     p->batches.push_back(T);
   }
   p->epoch = (uint64_t *)(base + epoch_off);
@@ -402,10 +400,9 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
       return WT_E_STATE;
     }
   }
-  if (progress) HIP_OR(p, launch_progress_begin(p->epoch, user));
   if (!p->pipeline) {
-    HIP_OR(p, launch_batch(p->batches[p->direct_batch], user));
-    if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress, user));
+    HIP_OR(p, launch_batch(p->batches[p->direct_batch], user, p->device));
+    if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress, true, user));
     HIP_OR(p, hipEventRecord(p->ev_last, user));
     return WT_OK;
   }
@@ -439,8 +436,8 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
     if (r > 0) HIP_OR(p, hipStreamWaitEvent(s, p->ev_done[(r - 1) % D], 0));
   }
   if (p->direct_batch >= 0) {
-    HIP_OR(p, launch_batch(p->batches[p->direct_batch], p->s_prep));
-    if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress, p->s_prep));
+    HIP_OR(p, launch_batch(p->batches[p->direct_batch], p->s_prep, p->device));
+    if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress, true, p->s_prep));
   }
 
   for (size_t c = 0; c < L.chunks.size(); ++c) {
@@ -457,7 +454,7 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
       HIP_OR(p, hipStreamWaitEvent(p->s_prep, p->ev_rel[C.wait_for], 0));
     }
     // stage 2: preparation (one launch over the chunk's work list)
-    HIP_OR(p, launch_batch(p->batches[p->first_chunk_batch + c], p->s_prep));
+    HIP_OR(p, launch_batch(p->batches[p->first_chunk_batch + c], p->s_prep, p->device));
     HIP_OR(p, hipEventRecord(p->ev_prep[c], p->s_prep));
     if (staged) {
       // stage 3: staging -> destination region (the emulated one-sided write)
@@ -465,10 +462,10 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
       for (const DstCopy &d : C.dst_copies)
         HIP_OR(p, hipMemcpyAsync(p->dst + d.dst_off, p->staging + C.slot_off + d.stage_off, (size_t)d.bytes,
                                  out_kind, p->s_out));
-      if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress + unit_base + c, p->s_out));
+      if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress + unit_base + c, unit_base + c == 0, p->s_out));
       if (waited[c]) HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_out));
     } else {
-      if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress + unit_base + c, p->s_prep));
+      if (progress) HIP_OR(p, launch_progress_mark(p->epoch, p->progress + unit_base + c, unit_base + c == 0, p->s_prep));
       if (waited[c]) HIP_OR(p, hipEventRecord(p->ev_rel[c], p->s_prep));
     }
   }
@@ -484,64 +481,6 @@ wt_status prepare_impl(wt_plan *p, hipStream_t user) {
 }  // namespace
 
 extern "C" {
-
-void wt_plan_options_init(wt_plan_options *opts) {
-  if (!opts) return;
-  std::memset(opts, 0, sizeof *opts);
-  opts->watermark_bytes = 512ull << 20;
-  opts->chunk_bytes = 0;
-  opts->dst_write_mode = WT_DST_ZERO_COPY;
-  opts->device = -1;
-}
-
-wt_status wt_plan_check(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, int32_t dst_kind,
-                        const wt_plan_options *opts, wt_plan_info *info) {
-  try {
-    const wt_plan_options o = resolve_opts(opts);
-    Layout L;
-    std::string err;
-    wt_status st = build_layout(tasks, n_tasks, dst_bytes, dst_kind, o, &L, &err);
-    if (st != WT_OK) {
-      set_err(nullptr, err);
-      return st;
-    }
-    if (info) *info = L.info;
-    return WT_OK;
-  } catch (const std::bad_alloc &) {
-    set_err(nullptr, "host allocation failed");
-    return WT_E_NOMEM;
-  } catch (...) {
-    set_err(nullptr, "internal error");
-    return WT_E_INVAL;
-  }
-}
-
-wt_status wt_plan_schedule(const wt_task *tasks, size_t n_tasks, size_t dst_bytes, int32_t dst_kind,
-                           const wt_plan_options *opts, wt_sched_op *ops, size_t max_ops, size_t *n_ops) {
-  try {
-    if (!n_ops) return WT_E_INVAL;
-    const wt_plan_options o = resolve_opts(opts);
-    Layout L;
-    std::string err;
-    wt_status st = build_layout(tasks, n_tasks, dst_bytes, dst_kind, o, &L, &err);
-    if (st != WT_OK) {
-      set_err(nullptr, err);
-      return st;
-    }
-    std::vector<wt_sched_op> v;
-    schedule_ops(L, &v);
-    *n_ops = v.size();
-    if (ops)
-      for (size_t i = 0; i < v.size() && i < max_ops; ++i) ops[i] = v[i];
-    return WT_OK;
-  } catch (const std::bad_alloc &) {
-    set_err(nullptr, "host allocation failed");
-    return WT_E_NOMEM;
-  } catch (...) {
-    set_err(nullptr, "internal error");
-    return WT_E_INVAL;
-  }
-}
 
 static wt_status plan_create(const wt_task *tasks, size_t n_tasks, void *dst, size_t dst_bytes, int32_t dst_kind,
                              const wt_plan_options *opts, bool noalloc, wt_plan **out) {
@@ -741,23 +680,6 @@ wt_status wt_quantize_act_b128(const void *x, int64_t n_rows, int64_t cols, int6
   return WT_OK;
 }
 
-wt_status wt_progress_wait(const uint64_t *word, uint64_t target, uint64_t timeout_ns) {
-  if (!word) return WT_E_INVAL;
-  const auto t0 = std::chrono::steady_clock::now();
-  for (uint32_t spin = 0;; ++spin) {
-    if (__atomic_load_n(word, __ATOMIC_ACQUIRE) >= target) return WT_OK;
-    if ((spin & 255u) == 0) {
-      const auto dt = std::chrono::steady_clock::now() - t0;
-      if ((uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(dt).count() >= timeout_ns) {
-        return __atomic_load_n(word, __ATOMIC_ACQUIRE) >= target ? WT_OK : WT_E_TIMEOUT;
-      }
-    }
-#if defined(__x86_64__)
-    __builtin_ia32_pause();
-#endif
-  }
-}
-
 void wt_plan_destroy(wt_plan *plan) {
   if (!plan) return;
   {
@@ -765,29 +687,6 @@ void wt_plan_destroy(wt_plan *plan) {
     destroy_resources(plan);
   }
   delete plan;
-}
-
-const char *wt_status_str(int status) {
-  switch (status) {
-    case WT_OK: return "WT_OK";
-    case WT_E_INVAL: return "WT_E_INVAL: malformed task table or argument";
-    case WT_E_RANGE: return "WT_E_RANGE: range outside the destination region or allocation";
-    case WT_E_OVERLAP: return "WT_E_OVERLAP: destination ranges overlap";
-    case WT_E_ALIGN: return "WT_E_ALIGN: misaligned pointer or offset";
-    case WT_E_NOMEM: return "WT_E_NOMEM: allocation failed";
-    case WT_E_HIP: return "WT_E_HIP: HIP runtime error";
-    case WT_E_WATERMARK: return "WT_E_WATERMARK: watermark below one output's staging need";
-    case WT_E_STATE: return "WT_E_STATE: plan busy";
-    case WT_E_TIMEOUT: return "WT_E_TIMEOUT: progress word did not reach its target in time";
-    default: return "unknown status";
-  }
-}
-
-const char *wt_plan_last_error(const wt_plan *plan) {
-  if (!plan) return g_last_error.c_str();
-  std::lock_guard<std::mutex> g(plan->err_mu);
-  // the string lives in the plan; valid until the next error on it or destroy
-  return plan->last_error.c_str();
 }
 
 wt_status wt_quantize_domain(const uint16_t *amax_bits, int64_t n_amax, int32_t path, uint8_t *out, void *stream) {

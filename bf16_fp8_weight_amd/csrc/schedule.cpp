@@ -16,7 +16,7 @@
 #include "wt_internal.h"
 
 namespace wt {
-void set_thread_error(const std::string &msg);  // runtime.cpp
+void set_thread_error(const std::string &msg);  // host_api.cpp
 }
 
 struct wt_schedule {

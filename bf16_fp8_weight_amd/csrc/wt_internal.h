@@ -111,6 +111,11 @@ struct LaunchTables {
   uint32_t n_edge;
   uint32_t n_general;
   uint32_t n_copies;
+  // 1: aligned-path work items go to XCDs in contiguous ranges (set when an
+  // output's rows do not start on 128-byte lines, so that neighbouring tiles
+  // share lines)
+  uint32_t xcd_order;
+  uint32_t pad;
 };
 
 // Arguments of the block-scaled activation quantization (one launch).
