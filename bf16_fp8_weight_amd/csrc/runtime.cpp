@@ -133,6 +133,18 @@ struct DeviceGuard {
 // no-allocation call on that device).
 static __device__ __align__(256) uint8_t scratch[WT_NOALLOC_TABLE_BYTES];
 
+// Flags of the event a replay of a plan without a pipeline records behind
+// its launch when the destination is device memory. The event only tells
+// wt_plan_destroy that every replay has run (the kernels read the device
+// tables; nothing the host reads depends on it), so it carries no
+// system-scope fence: with the fence (a cache write-back and invalidation) a
+// replay of a one-layer plan (720 tiles) took 9.75 us on the stream and
+// 5.6 us on the host back to back, without it 7.9 and 4.5 us, on MI355X.
+// Plans that write host memory keep the fenced event, the last command of
+// their replay, so that synchronizing with the stream still publishes the
+// bytes to the host as before.
+constexpr unsigned kReplayEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+
 struct NoAllocDev {
   std::once_flag once;
   hipError_t err = hipSuccess;
@@ -366,7 +378,8 @@ wt_status create_impl(wt_plan *p, const wt_task *tasks, size_t n_tasks, const wt
   if (p->noalloc)
     p->ev_last = p->noalloc->ev;
   else if (!p->pipeline)
-    HIP_OR(p, hipEventCreateWithFlags(&p->ev_last, hipEventDisableTiming));
+    HIP_OR(p, hipEventCreateWithFlags(&p->ev_last, p->dst_kind == WT_MEM_DEVICE ? kReplayEventFlags
+                                                                             : hipEventDisableTiming));
   if (p->pipeline) {
     HIP_OR(p, hipStreamCreateWithFlags(&p->s_h2d, hipStreamNonBlocking));
     HIP_OR(p, hipStreamCreateWithFlags(&p->s_prep, hipStreamNonBlocking));

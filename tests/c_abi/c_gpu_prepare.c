@@ -10,13 +10,18 @@
  * uint64 dst_offset, uint64 scale_offset, int64 rows[n_shards]; then the
  * shards' bytes (2 rows cols each), task by task, shard by shard.
  *
- * Usage: c_gpu_prepare IN OUT. Exit code 0 and "c gpu prepare ok" on
- * success; otherwise the failing call and its status text are printed. */
+ * Usage: c_gpu_prepare IN OUT [REPLAYS]. REPLAYS (default 2, at least 2)
+ * replays are made; from the second on they are issued back to back and
+ * timed, on the stream (HIP events) and on the host (the wt_prepare calls),
+ * and the times per replay are printed. Exit code 0 and "c gpu prepare ok"
+ * on success; otherwise the failing call and its status text are printed. */
+#define _POSIX_C_SOURCE 199309L
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #include "wt.h"
 
@@ -36,7 +41,9 @@
 static int read_exact(FILE *f, void *p, size_t n) { return fread(p, 1, n, f) == n; }
 
 int main(int argc, char **argv) {
-  if (argc != 3) FAIL("usage: %s IN OUT", argv[0]);
+  if (argc != 3 && argc != 4) FAIL("usage: %s IN OUT [REPLAYS]", argv[0]);
+  const long replays = argc == 4 ? strtol(argv[3], NULL, 10) : 2;
+  if (replays < 2 || replays > 1000000) FAIL("REPLAYS must be in [2, 1000000]");
   FILE *in = fopen(argv[1], "rb");
   if (!in) FAIL("cannot open %s", argv[1]);
 
@@ -100,11 +107,30 @@ int main(int argc, char **argv) {
   wt_plan_info info;
   st = wt_plan_get_info(plan, &info);
   if (st != WT_OK) FAIL("wt_plan_get_info: %s", wt_status_str(st));
-  for (int r = 0; r < 2; ++r) {
+  /* the first replay, then the others back to back, timed */
+  st = wt_prepare(plan, (void *)stream);
+  if (st != WT_OK) FAIL("wt_prepare: %s: %s", wt_status_str(st), wt_plan_last_error(plan));
+  HIP_CHECK(hipStreamSynchronize(stream));
+  hipEvent_t e0, e1;
+  HIP_CHECK(hipEventCreate(&e0));
+  HIP_CHECK(hipEventCreate(&e1));
+  struct timespec h0, h1;
+  clock_gettime(CLOCK_MONOTONIC, &h0);
+  HIP_CHECK(hipEventRecord(e0, stream));
+  for (long r = 1; r < replays; ++r) {
     st = wt_prepare(plan, (void *)stream);
     if (st != WT_OK) FAIL("wt_prepare: %s: %s", wt_status_str(st), wt_plan_last_error(plan));
   }
-  HIP_CHECK(hipStreamSynchronize(stream));
+  clock_gettime(CLOCK_MONOTONIC, &h1);
+  HIP_CHECK(hipEventRecord(e1, stream));
+  HIP_CHECK(hipEventSynchronize(e1));
+  float ms = 0.0f;
+  HIP_CHECK(hipEventElapsedTime(&ms, e0, e1));
+  const double host_us = (double)(h1.tv_sec - h0.tv_sec) * 1e6 + (double)(h1.tv_nsec - h0.tv_nsec) * 1e-3;
+  printf("%ld replays back to back: %.2f us per replay on the stream, %.2f us per wt_prepare call on the host\n",
+         replays - 1, 1000.0 * ms / (double)(replays - 1), host_us / (double)(replays - 1));
+  HIP_CHECK(hipEventDestroy(e0));
+  HIP_CHECK(hipEventDestroy(e1));
   wt_plan_destroy(plan);
 
   unsigned char *out = malloc((size_t)dst_bytes);

@@ -1,8 +1,8 @@
 """The plain-C program tests/c_abi/c_gpu_prepare (C99 + the HIP runtime +
 libwt.so, built by the repository's build step) drives the whole GPU path
 through the C ABI with no Python in its process: shards in device memory,
-wt_plan_create, two wt_prepare replays, wt_plan_destroy. The destination
-image it writes must equal the oracle's bit for bit. Marked gpu."""
+wt_plan_create, wt_prepare replays, wt_plan_destroy. The destination image
+it writes must equal the oracle's bit for bit. Marked gpu."""
 import os
 import struct
 import subprocess
@@ -56,4 +56,21 @@ def test_c_program_matches_oracle(tmp_path, make):
     assert r.returncode == 0 and "c gpu prepare ok" in r.stdout, r.stdout + r.stderr
     got = np.fromfile(out, dtype=np.uint8)
     assert got.size == wl.dst_bytes
+    assert_images_equal(got, oracle_image_threaded(wl), wl)
+
+
+def test_c_program_back_to_back_replays(tmp_path):
+    # 2,000 replays of the one-layer plan issued back to back from C: the
+    # image is still the oracle's, and the time per replay on the stream and
+    # per call on the host is reported (the library's replay cost without
+    # Python or timing events between the calls)
+    assert os.path.exists(EXE), "tests/c_abi/c_gpu_prepare is not built (run the build step)"
+    wl = W.dense_layer_h1024(device="cpu")
+    inp, out = tmp_path / "in.bin", tmp_path / "out.bin"
+    _write_input(wl, inp)
+    r = subprocess.run([EXE, str(inp), str(out), "2001"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "c gpu prepare ok" in r.stdout, r.stdout + r.stderr
+    print(r.stdout.strip(), flush=True)
+    assert "2000 replays back to back" in r.stdout
+    got = np.fromfile(out, dtype=np.uint8)
     assert_images_equal(got, oracle_image_threaded(wl), wl)
