@@ -136,6 +136,37 @@ def test_new_contents_same_plan():
         wt.wt_plan_destroy(h)
 
 
+def test_consumers_on_the_replay_stream_see_the_bytes():
+    # work enqueued on the replay's stream right behind it sees the new bytes
+    # with only that stream synchronized: a device-to-host copy into pinned
+    # memory and a device-side clone, while the contents change every step
+    from bf16_fp8_weight_amd import wt
+    wl = W.custom([(384, 1024), (256, 256), (129, 40)], n_shards=4, device="cuda")
+    dst = torch.full((wl.dst_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    host = torch.empty(wl.dst_bytes, dtype=torch.uint8, pin_memory=True)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    h = wt.wt_plan_create(wt.task_table(wl), dst.data_ptr(), wl.dst_bytes)
+    try:
+        for step in range(4):
+            g = torch.Generator(device="cuda").manual_seed(200 + step)
+            with torch.cuda.stream(s):
+                for o in wl.outputs:
+                    for p in o.parts:
+                        for sh in p.shards:
+                            sh.copy_((torch.randn(sh.shape, generator=g, device="cuda") * (0.02 * (step + 1)))
+                                     .to(torch.bfloat16))
+                wt.wt_prepare(h, s.cuda_stream)
+                host.copy_(dst, non_blocking=True)
+                clone = dst.clone()
+            s.synchronize()
+            want = oracle_image_threaded(wl)
+            assert_images_equal(host.numpy(), want, wl)
+            assert_images_equal(clone.cpu().numpy(), want, wl)
+    finally:
+        wt.wt_plan_destroy(h)
+
+
 @pytest.mark.parametrize("host", [False, True])
 def test_destroy_right_after_prepare(host):
     # destroy waits for the plan's enqueued work (the launch on the caller's
